@@ -1,0 +1,288 @@
+"""Seeded synthetic inputs for sink attention.
+
+This module only draws and lays out inputs: lengths, page tables, Q/K/V and
+per-head sinks.  It holds none of the attention arithmetic, so the oracle and
+the GPU library can both consume what it produces.
+
+Recipe (every workload):
+  * generator: numpy ``default_rng(seed)`` (PCG64);
+  * draw order: (1) lengths, (2) page permutation, (3) Q, (4) K, (5) V,
+    (6) sinks;
+  * Q, K and V are drawn fp32 ~ N(0, 1), then rounded once to bf16
+    (round-to-nearest-even) on the host; both sides read those bits;
+  * a paged cache holds exactly sum(ceil(L_b / page_size)) pages whose ids
+    are a random permutation of the pool, handed out in request order, so
+    the pages of different requests interleave in memory;
+  * the unused slots of a request's last page hold finite poison
+    (K = 8.0, V = 100.0): a kernel that reads past the end of a request
+    lets those keys dominate its softmax, so the error is large.
+
+Layouts (the library's documented format):
+  q       bf16 bits uint16 [total_q, Hq, D]; qo_indptr int32 [B+1]
+  contiguous k/v  uint16 [total_kv, Hkv, D]; kv_indptr = token offsets
+  paged k/v       uint16 [num_pages, Hkv, page_size, D];
+                  kv_indptr = offsets into page_indices (int32)
+  kv_len  int32 [B];  sinks fp32 [Hq] or None (no sink)
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "Batch", "Mixed", "to_bf16_bits", "bf16_bits_to_f32", "make_batch",
+    "config", "CONFIG_NAMES", "K_POISON", "V_POISON",
+]
+
+K_POISON = 8.0
+V_POISON = 100.0
+PAGE_SIZE = 16
+HEAD_DIM = 64
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> the fp32 values they denote (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass
+class Batch:
+    """One call's worth of inputs (prefill or decode)."""
+    kind: str                       # "prefill" or "decode"
+    q: np.ndarray                   # uint16 [total_q, Hq, D]
+    qo_indptr: np.ndarray           # int32 [B+1]
+    k: np.ndarray                   # uint16, contiguous or paged (see module doc)
+    v: np.ndarray
+    kv_indptr: np.ndarray           # int32 [B+1]
+    page_indices: Optional[np.ndarray]  # int32 [nnz] or None (contiguous)
+    kv_len: np.ndarray              # int32 [B]
+    sinks: Optional[np.ndarray]     # float32 [Hq] or None
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    sm_scale: float
+    causal: bool
+    out_dtype: str = "bf16"         # "bf16" or "f32"
+    num_splits: int = 0             # decode: 0 = library's automatic plan
+    name: str = ""
+
+    @property
+    def batch(self) -> int:
+        return int(self.kv_len.shape[0])
+
+    @property
+    def total_q(self) -> int:
+        return int(self.qo_indptr[-1])
+
+    @property
+    def qlens(self) -> np.ndarray:
+        return np.diff(self.qo_indptr)
+
+    @property
+    def max_qlen(self) -> int:
+        return int(self.qlens.max()) if self.batch else 0
+
+    @property
+    def max_kv_len(self) -> int:
+        return int(self.kv_len.max()) if self.batch else 0
+
+    @property
+    def paged(self) -> bool:
+        return self.page_indices is not None
+
+
+@dataclasses.dataclass
+class Mixed:
+    """A chunked-prefill call and a decode call over one shared page pool."""
+    prefill: Batch
+    decode: Batch
+    name: str = ""
+
+
+def _draw_qkv_pool(rng, shape_q, shape_kv):
+    q = to_bf16_bits(rng.standard_normal(shape_q, dtype=np.float32))
+    k = _normal_bf16(rng, shape_kv)
+    v = _normal_bf16(rng, shape_kv)
+    return q, k, v
+
+
+def _normal_bf16(rng, shape, chunk_elems: int = 1 << 26) -> np.ndarray:
+    """N(0,1) fp32 draws rounded to bf16, generated in chunks to bound memory."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, chunk_elems):
+        e = min(n, s + chunk_elems)
+        out[s:e] = to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+    return out.reshape(shape)
+
+
+def _poison_tails(k, v, page_indices, kv_indptr, kv_len, page_size):
+    """Fill the unused slots of each request's last page with poison."""
+    kp, vp = to_bf16_bits(np.float32(K_POISON)), to_bf16_bits(np.float32(V_POISON))
+    for b in range(kv_len.shape[0]):
+        L = int(kv_len[b])
+        used = L % page_size
+        n_pages = int(kv_indptr[b + 1] - kv_indptr[b])
+        if n_pages == 0:
+            continue
+        if used == 0 and L > 0:
+            continue
+        last = int(page_indices[kv_indptr[b + 1] - 1])
+        k[last, :, used:, :] = kp
+        v[last, :, used:, :] = vp
+
+
+def _draw_sinks(rng, hq: int, sinks, std: float = 1.0) -> Optional[np.ndarray]:
+    if sinks is None or sinks is False:
+        return None
+    if isinstance(sinks, str) and sinks == "normal":
+        return (std * rng.standard_normal(hq)).astype(np.float32)
+    arr = np.asarray(sinks, dtype=np.float32)
+    if arr.ndim == 0:
+        return np.full(hq, float(arr), dtype=np.float32)
+    assert arr.shape == (hq,)
+    return arr.copy()
+
+
+def make_batch(seed, *, kind: str, qlens: Sequence[int], kv_lens: Sequence[int],
+               hq: int, hkv: int, d: int = HEAD_DIM, paged: bool = False,
+               page_size: int = PAGE_SIZE, sinks="normal", sink_std: float = 1.0,
+               causal: bool = True, out_dtype: str = "bf16", num_splits: int = 0,
+               sm_scale: Optional[float] = None, permute_pages: bool = True,
+               name: str = "") -> Batch:
+    """Draw one batch.  `seed` is an int or a numpy Generator that has already
+    drawn the lengths (step 1); `qlens`/`kv_lens` are given and the remaining
+    draws follow the recipe order."""
+    rng = seed if isinstance(seed, np.random.Generator) else np.random.default_rng(seed)
+    qlens = np.asarray(qlens, dtype=np.int64)
+    kv_lens = np.asarray(kv_lens, dtype=np.int64)
+    B = qlens.shape[0]
+    assert kv_lens.shape == (B,)
+    if causal:
+        assert np.all(qlens <= kv_lens), "a causal query must have its own key"
+    qo_indptr = np.zeros(B + 1, dtype=np.int32)
+    qo_indptr[1:] = np.cumsum(qlens)
+    total_q = int(qo_indptr[-1])
+    if paged:
+        pages_per = (kv_lens + page_size - 1) // page_size
+        kv_indptr = np.zeros(B + 1, dtype=np.int32)
+        kv_indptr[1:] = np.cumsum(pages_per)
+        n_pages = int(kv_indptr[-1])
+        page_indices = (rng.permutation(n_pages) if permute_pages
+                        else np.arange(n_pages)).astype(np.int32)
+        q, k, v = _draw_qkv_pool(rng, (total_q, hq, d), (max(n_pages, 1), hkv, page_size, d))
+        _poison_tails(k, v, page_indices, kv_indptr, kv_lens, page_size)
+    else:
+        kv_indptr = np.zeros(B + 1, dtype=np.int32)
+        kv_indptr[1:] = np.cumsum(kv_lens)
+        page_indices = None
+        q, k, v = _draw_qkv_pool(rng, (total_q, hq, d), (max(int(kv_indptr[-1]), 1), hkv, d))
+    s = _draw_sinks(rng, hq, sinks, sink_std)
+    return Batch(kind=kind, q=q, qo_indptr=qo_indptr, k=k, v=v, kv_indptr=kv_indptr,
+                 page_indices=page_indices, kv_len=kv_lens.astype(np.int32), sinks=s,
+                 num_qo_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=page_size,
+                 sm_scale=(1.0 / math.sqrt(d)) if sm_scale is None else float(sm_scale),
+                 causal=causal, out_dtype=out_dtype, num_splits=num_splits, name=name)
+
+
+CONFIG_NAMES = {
+    1: "c1 tiny causal prefill: B=1 x 128, 4q/1kv, d=64, fp32 out",
+    2: "c2 paged decode: B=64, L~U[1,4096], 64q/8kv, d=64, page 16",
+    3: "c3 split-KV decode: B=4, L=131072, 64q/8kv, d=64, page 16, 32 splits",
+    4: "c4 causal prefill: B=8 x 4096, 64q/8kv, d=64, contiguous KV",
+    5: "c5 mixed: 16 chunked prefills (n~U[256,2048], prefix~U[0,8192]) + "
+       "256 decodes (L~U[1,16384]), 64q/8kv, d=64, page 16",
+}
+
+
+def config(n: int, seed: Optional[int] = None):
+    """The five workloads with their seeded recipes (seed = 1000 + n)."""
+    seed = 1000 + n if seed is None else seed
+    if n == 1:
+        return make_batch(seed, kind="prefill", qlens=[128], kv_lens=[128], hq=4, hkv=1,
+                          causal=True, out_dtype="f32", name=CONFIG_NAMES[1])
+    if n == 2:
+        rng = np.random.default_rng(seed)
+        L = rng.integers(1, 4096, size=64, endpoint=True)
+        return make_batch(rng, kind="decode", qlens=[1] * 64, kv_lens=L, hq=64, hkv=8,
+                          paged=True, causal=True, name=CONFIG_NAMES[2])
+    if n == 3:
+        return make_batch(seed, kind="decode", qlens=[1] * 4, kv_lens=[131072] * 4, hq=64,
+                          hkv=8, paged=True, sink_std=2.0, num_splits=32, name=CONFIG_NAMES[3])
+    if n == 4:
+        return make_batch(seed, kind="prefill", qlens=[4096] * 8, kv_lens=[4096] * 8, hq=64,
+                          hkv=8, paged=False, causal=True, name=CONFIG_NAMES[4])
+    if n == 5:
+        return mixed(seed)
+    raise ValueError(f"no workload {n}")
+
+
+def c5_sinks(rng, hq: int = 64) -> np.ndarray:
+    """N(0,1) sinks with the extremes of workload 5 planted on fixed heads."""
+    s = rng.standard_normal(hq).astype(np.float32)
+    for h in (0, 17, 42):
+        if h < hq:
+            s[h] = -1e4
+    for h in (5, 31, 63):
+        if h < hq:
+            s[h] = 10.0
+    return s
+
+
+def mixed(seed: int = 1005, n_prefill: int = 16, n_decode: int = 256, hq: int = 64,
+          hkv: int = 8, scale: float = 1.0) -> Mixed:
+    """Workload 5: chunked prefills on cached prefixes plus decodes, one page
+    pool.  `scale` < 1 shrinks every length (for fast parity cases)."""
+    rng = np.random.default_rng(seed)
+    n_new = rng.integers(256, 2048, size=n_prefill, endpoint=True)
+    prefix = rng.integers(0, 8192, size=n_prefill, endpoint=True)
+    dec_L = rng.integers(1, 16384, size=n_decode, endpoint=True)
+    if scale != 1.0:
+        n_new = np.maximum(1, (n_new * scale).astype(np.int64))
+        prefix = (prefix * scale).astype(np.int64)
+        dec_L = np.maximum(1, (dec_L * scale).astype(np.int64))
+    pf_kv = prefix + n_new
+    all_L = np.concatenate([pf_kv, dec_L])
+    ps = PAGE_SIZE
+    pages_per = (all_L + ps - 1) // ps
+    indptr_all = np.zeros(all_L.shape[0] + 1, dtype=np.int64)
+    indptr_all[1:] = np.cumsum(pages_per)
+    n_pages = int(indptr_all[-1])
+    perm = rng.permutation(n_pages).astype(np.int32)
+    d = HEAD_DIM
+    total_q_pf = int(n_new.sum())
+    q_pf = to_bf16_bits(rng.standard_normal((total_q_pf, hq, d), dtype=np.float32))
+    q_dec = to_bf16_bits(rng.standard_normal((n_decode, hq, d), dtype=np.float32))
+    k = _normal_bf16(rng, (n_pages, hkv, ps, d))
+    v = _normal_bf16(rng, (n_pages, hkv, ps, d))
+    _poison_tails(k, v, perm, indptr_all, all_L, ps)
+    sinks = c5_sinks(rng, hq)
+
+    pf_pages = int(indptr_all[n_prefill])
+    pf_indptr = indptr_all[: n_prefill + 1].astype(np.int32)
+    dec_indptr = (indptr_all[n_prefill:] - pf_pages).astype(np.int32)
+    qo_pf = np.zeros(n_prefill + 1, dtype=np.int32)
+    qo_pf[1:] = np.cumsum(n_new)
+    scale_attn = 1.0 / math.sqrt(d)
+    pre = Batch(kind="prefill", q=q_pf, qo_indptr=qo_pf, k=k, v=v, kv_indptr=pf_indptr,
+                page_indices=perm[:pf_pages].copy(), kv_len=pf_kv.astype(np.int32), sinks=sinks,
+                num_qo_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=ps,
+                sm_scale=scale_attn, causal=True, name="c5 chunked prefill part")
+    dec = Batch(kind="decode", q=q_dec, qo_indptr=np.arange(n_decode + 1, dtype=np.int32),
+                k=k, v=v, kv_indptr=dec_indptr, page_indices=perm[pf_pages:].copy(),
+                kv_len=dec_L.astype(np.int32), sinks=sinks, num_qo_heads=hq, num_kv_heads=hkv,
+                head_dim=d, page_size=ps, sm_scale=scale_attn, causal=True,
+                name="c5 decode part")
+    return Mixed(prefill=pre, decode=dec, name=CONFIG_NAMES[5])
