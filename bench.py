@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the sink-attention hot path on one MI355X.
+
+Default workload: paged decode, batch 64, KV lengths uniform in [1, 4096],
+64 query / 8 KV heads, head_dim 64, 16-token pages with a permuted page table
+(the decode workload the headline metric is quoted on).  One step = one
+pass of the decode path: the split-KV partial kernel
+(sink_attn_decode_partial) followed by the LSE merge (sink_attn_merge), both
+through the C ABI.  Metric: KV bytes read per second (2 * Hkv * 64 * 2 B per
+KV token) over the whole step.
+
+Also reported, on the same JSON line:
+  * "roofline": the dominant kernel (decode partial) -- algorithmic bytes
+    per launch / its mean launch time from HIP events on its own stream,
+    against the 8 TB/s HBM peak; "traffic" from rocprofv3 counters when a
+    measurement for the current kernel exists, else null;
+  * "prefill": the causal prefill workload (8 x 4096 tokens, 64/8 heads,
+    contiguous KV) in TFLOP/s against the 2.5 PFLOP/s dense bf16 peak;
+  * "cpu_baseline": the fp64 oracle timed on this host's cores on the same
+    decode batch.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+KV_COPIES = 4                  # rotated KV pools: 4 x 269 MB > 256 MB last-level cache
+
+# HBM bytes per dispatch measured with rocprofv3 counters for the current
+# decode-partial kernel on this workload (None until measured).
+DECODE_TRAFFIC_BYTES = None
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def decode_algorithmic_bytes(b) -> int:
+    """Bytes the definition must read once: K and V of every KV token
+    (2 * Hkv * D * 2 B each), the queries, page ids and per-request lengths."""
+    L = b.kv_len.astype(np.int64)
+    kv = int(L.sum()) * 2 * b.num_kv_heads * b.head_dim * 2
+    q = b.batch * b.num_qo_heads * b.head_dim * 2
+    pages = int(((L + b.page_size - 1) // b.page_size).sum()) * 4
+    return kv + q + pages + b.batch * 8
+
+
+def prefill_pairs(b) -> int:
+    """Unmasked (query row, head, key) triples of a causal prefill."""
+    qlens = np.diff(b.qo_indptr).astype(np.int64)
+    kvl = b.kv_len.astype(np.int64)
+    # query t sees keys 0 .. kv_len - qlen + t  ->  sum_t (kv_len - qlen + t + 1)
+    per_req = qlens * (kvl - qlens) + qlens * (qlens + 1) // 2
+    return int(per_req.sum()) * b.num_qo_heads
+
+
+def bench_decode(args, torch, sa, device, W):
+    b = W.config(2)
+    db = device.to_device(b)
+    S = device.splits_of(db)
+    B, Hq, D = db.batch, db.num_qo_heads, db.head_dim
+    o_parts = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
+    lse_parts = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    ks = [db.k] + [db.k.clone() for _ in range(KV_COPIES - 1)]
+    vs = [db.v] + [db.v.clone() for _ in range(KV_COPIES - 1)]
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        k, v = ks[i % KV_COPIES], vs[i % KV_COPIES]
+        if ev is not None:
+            ev[0].record()
+        sa.sink_attn_decode_partial(db.q, k, v, db.kv_indptr, db.page_indices, db.kv_len, db.sinks,
+                                    B, Hq, db.num_kv_heads, D, db.page_size, db.max_kv_len,
+                                    db.num_splits, db.sm_scale, o_parts, lse_parts)
+        if ev is not None:
+            ev[1].record()
+        sa.sink_attn_merge(o_parts, lse_parts, B, Hq, S, D, db.out, sa.BF16, db.lse)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    kern_ms = float(np.mean([a.elapsed_time(c) for a, c in evs]))
+    kv_bytes = int(b.kv_len.astype(np.int64).sum()) * 2 * b.num_kv_heads * b.head_dim * 2
+    alg = decode_algorithmic_bytes(b)
+    ms_step = total_ms / args.steps
+    res = dict(batch=b, db=db, S=S, ms_step=ms_step, kern_ms=kern_ms, kv_bytes=kv_bytes,
+               alg_bytes=alg, value=kv_bytes / (ms_step * 1e-3) / 1e9)
+    return res
+
+
+def bench_prefill(args, torch, sa, device, W):
+    b = W.config(4)
+    db = device.to_device(b, with_lse=False)
+    torch.cuda.synchronize()
+    steps = max(5, min(args.steps, 20))
+    for _ in range(max(1, args.warmup)):
+        device.run(db)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        device.run(db)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(c) for a, c in evs]))
+    flops = prefill_pairs(b) * 4 * b.head_dim
+    tfs = flops / (ms * 1e-3) / 1e12
+    return dict(workload=W.CONFIG_NAMES[4], value=round(tfs, 2), unit="TFLOP/s",
+                ms_per_call=round(ms, 4), flop_per_call=flops, steps=steps,
+                roofline=dict(bound="mfma", achieved=round(tfs, 2), peak=BF16_PEAK_TFLOPS,
+                              unit="TFLOP/s", frac=round(tfs / BF16_PEAK_TFLOPS, 4),
+                              traffic=None))
+
+
+def cpu_baseline(b, kv_bytes, seconds):
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    times = []
+    t_end = time.perf_counter() + seconds
+    while True:
+        t = time.perf_counter()
+        oracle.attend(b, nthreads=threads)
+        times.append(time.perf_counter() - t)
+        if time.perf_counter() >= t_end or len(times) >= 50:
+            break
+    mean = float(np.mean(times))
+    return dict(value=round(kv_bytes / mean / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
+                sample=f"the whole decode batch (64 requests, {int(b.kv_len.sum())} KV tokens, "
+                       f"all 64 heads), fp64, {len(times)} run(s), mean {mean:.3f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus "
+              f"{args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        sys.exit("--steps must be >= 1")
+
+    import torch
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    import gqa_attention_sinks_attn_amd as sa
+    from gqa_attention_sinks_attn_amd import device
+    import workloads as W
+
+    log("[bench] decode workload: generating inputs")
+    dec = bench_decode(args, torch, sa, device, W)
+    log(f"[bench] decode: {dec['ms_step']:.4f} ms/step, kernel {dec['kern_ms']:.4f} ms")
+    pre = None
+    if not args.no_prefill:
+        log("[bench] prefill workload: generating inputs")
+        pre = bench_prefill(args, torch, sa, device, W)
+        log(f"[bench] prefill: {pre['ms_per_call']} ms, {pre['value']} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(dec["batch"], dec["kv_bytes"], args.cpu_seconds)
+
+    b = dec["batch"]
+    achieved = dec["alg_bytes"] / (dec["kern_ms"] * 1e-3) / 1e9
+    line = {
+        "metric": "sink-GQA prefill TFLOP/s and decode KV GB/s at 1 MI355X, % of roofline",
+        "value": round(dec["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": W.CONFIG_NAMES[2],
+            "batch": b.batch, "kv_tokens": int(b.kv_len.sum()), "num_qo_heads": b.num_qo_heads,
+            "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "page_size": b.page_size,
+            "num_splits": dec["S"], "kv_copies_rotated": KV_COPIES,
+            "step": "sink_attn_decode_partial + sink_attn_merge",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": DECODE_TRAFFIC_BYTES,
+            "kernel": "decode_kernel<8> (split-KV partial)",
+            "kernel_ms": round(dec["kern_ms"], 5), "algorithmic_bytes": dec["alg_bytes"],
+        },
+        "cpu_baseline": cpu,
+    }
+    if pre is not None:
+        line["prefill"] = pre
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,354 @@
+// C ABI of the sink-attention library: argument validation, the decode
+// split planner, and dispatch to the gfx950 kernels.  Declarations and the
+// contract of every entry point are in include/sink_attn.h.
+#include "sink_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+sink_attn_status fail(sink_attn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+sink_attn_status ok() {
+  g_last_error[0] = '\0';
+  return SINK_ATTN_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kHeadDim = 64;
+constexpr int kPageSize = 16;
+
+sink_attn_status check_heads(int32_t hq, int32_t hkv, bool decode) {
+  if (hq <= 0 || hkv <= 0) return fail(SINK_ATTN_ERR_BAD_SHAPE, "head counts must be positive (Hq=%d, Hkv=%d)", hq, hkv);
+  if (hq % hkv) return fail(SINK_ATTN_ERR_BAD_SHAPE, "Hq=%d is not a multiple of Hkv=%d", hq, hkv);
+  const int G = hq / hkv;
+  const bool supported = G == 1 || G == 2 || G == 4 || G == 8 || (decode && G == 16);
+  if (!supported)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "group size Hq/Hkv=%d is not built (%s)", G,
+                decode ? "decode supports 1, 2, 4, 8, 16" : "prefill supports 1, 2, 4, 8");
+  return ok();
+}
+
+sink_attn_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Keys per split are rounded to whole pages.  The automatic plan aims at
+// several waves per compute unit across 256 CUs while keeping each split at
+// least 16 pages long, so that a workgroup amortises its merge.
+int32_t plan_splits(int32_t batch, int32_t hkv, int32_t max_kv_len, int32_t requested) {
+  const int32_t pages = (max_kv_len + kPageSize - 1) / kPageSize;
+  if (requested > 0) {
+    int32_t s = requested;
+    if (pages > 0 && s > pages) s = pages;  // never more splits than pages
+    return s < 1 ? 1 : s;
+  }
+  if (pages <= 16) return 1;
+  const int64_t units = (int64_t)batch * hkv;
+  const int64_t target_wgs = 2048;  // 8 workgroups (32 waves) per CU on 256 CUs
+  int64_t s = (target_wgs + units - 1) / units;
+  const int64_t max_by_len = (pages + 15) / 16;  // >= 16 pages per split
+  if (s > max_by_len) s = max_by_len;
+  if (s < 1) s = 1;
+  if (s > 256) s = 256;
+  return (int32_t)s;
+}
+
+int32_t chunk_pages_for(int32_t max_kv_len, int32_t splits) {
+  const int32_t pages = (max_kv_len + kPageSize - 1) / kPageSize;
+  int32_t cp = (pages + splits - 1) / splits;
+  return cp < 1 ? 1 : cp;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sink_attn_status_string(sink_attn_status s) {
+  switch (s) {
+    case SINK_ATTN_OK: return "ok";
+    case SINK_ATTN_ERR_NULL_ARG: return "a required pointer is NULL";
+    case SINK_ATTN_ERR_BAD_SHAPE: return "bad or inconsistent sizes";
+    case SINK_ATTN_ERR_UNSUPPORTED: return "configuration not supported";
+    case SINK_ATTN_ERR_MISALIGNED: return "misaligned pointer";
+    case SINK_ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case SINK_ATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* sink_attn_last_error(void) { return g_last_error; }
+
+const char* sink_attn_version(void) { return "sink_attn 0.1 gfx950"; }
+
+int32_t sink_attn_decode_num_splits(int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                    int32_t max_kv_len, int32_t num_splits) {
+  (void)num_qo_heads;
+  if (batch <= 0 || num_kv_heads <= 0 || max_kv_len < 0) return 1;
+  return plan_splits(batch, num_kv_heads, max_kv_len, num_splits);
+}
+
+size_t sink_attn_decode_workspace_size(int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t max_kv_len, int32_t num_splits) {
+  if (batch <= 0 || num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_kv_len < 0 ||
+      num_splits < 0)
+    return 0;
+  const int32_t s = plan_splits(batch, num_kv_heads, max_kv_len, num_splits);
+  if (s <= 1) return 0;
+  const size_t rows = (size_t)batch * num_qo_heads * s;
+  const size_t o_bytes = rows * head_dim * sizeof(float);
+  const size_t l_bytes = rows * sizeof(float);
+  return o_bytes + ((l_bytes + 255) / 256) * 256;
+}
+
+sink_attn_status sink_attn_prefill(const void* q, const int32_t* qo_indptr, const void* k,
+                                   const void* v, const int32_t* kv_indptr,
+                                   const int32_t* page_indices, const int32_t* kv_len,
+                                   const float* sinks, int32_t batch, int32_t num_qo_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                   int32_t total_q, int32_t max_qlen, int32_t max_kv_len,
+                                   float sm_scale, int32_t causal, void* out,
+                                   sink_attn_dtype out_dtype, float* lse, void* stream) {
+  if (!q || !qo_indptr || !k || !v || !kv_indptr || !out)
+    return fail(SINK_ATTN_ERR_NULL_ARG, "prefill: q, qo_indptr, k, v, kv_indptr and out are required");
+  if (page_indices && !kv_len)
+    return fail(SINK_ATTN_ERR_NULL_ARG, "prefill: kv_len is required with a paged cache");
+  if (batch <= 0 || total_q < 0 || max_qlen < 0 || max_kv_len < 0)
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "prefill: batch=%d total_q=%d max_qlen=%d max_kv_len=%d",
+                batch, total_q, max_qlen, max_kv_len);
+  if (max_qlen > total_q)
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "prefill: max_qlen=%d exceeds total_q=%d", max_qlen, total_q);
+  if (causal && max_qlen > 0 && max_kv_len <= 0)
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "prefill: causal queries need keys (max_kv_len=%d)", max_kv_len);
+  sink_attn_status st = check_heads(num_qo_heads, num_kv_heads, false);
+  if (st != SINK_ATTN_OK) return st;
+  if (head_dim != kHeadDim)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "prefill: head_dim=%d (only 64 is built)", head_dim);
+  if (page_indices && page_size != kPageSize)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "prefill: page_size=%d (only 16 is built)", page_size);
+  if (out_dtype != SINK_ATTN_BF16 && out_dtype != SINK_ATTN_F32)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "prefill: unknown out_dtype %d", (int)out_dtype);
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "prefill: sm_scale must be positive and finite");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(SINK_ATTN_ERR_MISALIGNED, "prefill: q, k, v and out must be 16-byte aligned");
+  if (!aligned(qo_indptr, 4) || !aligned(kv_indptr, 4) || (page_indices && !aligned(page_indices, 4)) ||
+      (kv_len && !aligned(kv_len, 4)) || (sinks && !aligned(sinks, 4)) || (lse && !aligned(lse, 4)))
+    return fail(SINK_ATTN_ERR_MISALIGNED, "prefill: index, sink and lse arrays must be 4-byte aligned");
+  if (total_q == 0 || max_qlen == 0) return ok();
+
+  sa::PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.qo_indptr = qo_indptr;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.kv_indptr = kv_indptr;
+  a.page_indices = page_indices;
+  a.kv_len = kv_len;
+  a.sinks = sinks;
+  a.batch = batch;
+  a.hq = num_qo_heads;
+  a.hkv = num_kv_heads;
+  a.max_qlen = max_qlen;
+  a.causal = causal ? 1 : 0;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.out = out;
+  a.out_f32 = out_dtype == SINK_ATTN_F32;
+  a.lse = lse;
+  return hip_status(sa::launch_prefill(a, num_qo_heads / num_kv_heads,
+                                       static_cast<hipStream_t>(stream)),
+                    "prefill launch");
+}
+
+sink_attn_status sink_attn_merge(const float* o_parts, const float* lse_parts, int32_t num_rows,
+                                 int32_t num_heads, int32_t num_splits, int32_t head_dim,
+                                 void* out, sink_attn_dtype out_dtype, float* lse_out,
+                                 void* stream) {
+  if (!o_parts || !lse_parts || !out)
+    return fail(SINK_ATTN_ERR_NULL_ARG, "merge: o_parts, lse_parts and out are required");
+  if (num_rows < 0 || num_heads <= 0 || num_splits <= 0)
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "merge: rows=%d heads=%d splits=%d", num_rows, num_heads,
+                num_splits);
+  if (head_dim != kHeadDim)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "merge: head_dim=%d (only 64 is built)", head_dim);
+  if (out_dtype != SINK_ATTN_BF16 && out_dtype != SINK_ATTN_F32)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "merge: unknown out_dtype %d", (int)out_dtype);
+  if (!aligned(o_parts, 16) || !aligned(out, 16))
+    return fail(SINK_ATTN_ERR_MISALIGNED, "merge: o_parts and out must be 16-byte aligned");
+  if (!aligned(lse_parts, 4) || (lse_out && !aligned(lse_out, 4)))
+    return fail(SINK_ATTN_ERR_MISALIGNED, "merge: lse arrays must be 4-byte aligned");
+  if (num_rows == 0) return ok();
+  sa::MergeArgs a;
+  a.o_parts = o_parts;
+  a.lse_parts = lse_parts;
+  a.rows = num_rows;
+  a.heads = num_heads;
+  a.splits = num_splits;
+  a.out = out;
+  a.out_f32 = out_dtype == SINK_ATTN_F32;
+  a.lse = lse_out;
+  return hip_status(sa::launch_merge(a, static_cast<hipStream_t>(stream)), "merge launch");
+}
+
+namespace {
+
+sink_attn_status check_decode_common(const void* q, const void* k_pages, const void* v_pages,
+                                     const int32_t* page_indptr, const int32_t* page_indices,
+                                     const int32_t* kv_len, const float* sinks, int32_t batch,
+                                     int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t page_size, int32_t max_kv_len, int32_t num_splits,
+                                     float sm_scale) {
+  if (!q || !k_pages || !v_pages || !page_indptr || !page_indices || !kv_len)
+    return fail(SINK_ATTN_ERR_NULL_ARG,
+                "decode: q, k_pages, v_pages, page_indptr, page_indices and kv_len are required");
+  if (batch <= 0 || max_kv_len < 0 || num_splits < 0)
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "decode: batch=%d max_kv_len=%d num_splits=%d", batch,
+                max_kv_len, num_splits);
+  sink_attn_status st = check_heads(num_qo_heads, num_kv_heads, true);
+  if (st != SINK_ATTN_OK) return st;
+  if (head_dim != kHeadDim)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "decode: head_dim=%d (only 64 is built)", head_dim);
+  if (page_size != kPageSize)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "decode: page_size=%d (only 16 is built)", page_size);
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "decode: sm_scale must be positive and finite");
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16))
+    return fail(SINK_ATTN_ERR_MISALIGNED, "decode: q, k_pages and v_pages must be 16-byte aligned");
+  if (!aligned(page_indptr, 4) || !aligned(page_indices, 4) || !aligned(kv_len, 4) ||
+      (sinks && !aligned(sinks, 4)))
+    return fail(SINK_ATTN_ERR_MISALIGNED, "decode: index and sink arrays must be 4-byte aligned");
+  return ok();
+}
+
+sa::DecodeArgs decode_args(const void* q, const void* k_pages, const void* v_pages,
+                           const int32_t* page_indptr, const int32_t* page_indices,
+                           const int32_t* kv_len, const float* sinks, int32_t batch,
+                           int32_t num_qo_heads, int32_t num_kv_heads, int32_t max_kv_len,
+                           int32_t S, float sm_scale) {
+  sa::DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_pages);
+  a.v = static_cast<const uint16_t*>(v_pages);
+  a.page_indptr = page_indptr;
+  a.page_indices = page_indices;
+  a.kv_len = kv_len;
+  a.sinks = sinks;
+  a.batch = batch;
+  a.hq = num_qo_heads;
+  a.hkv = num_kv_heads;
+  a.num_splits = S;
+  a.chunk_pages = chunk_pages_for(max_kv_len, S);
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.out = nullptr;
+  a.out_f32 = 0;
+  a.lse = nullptr;
+  a.o_part = nullptr;
+  a.lse_part = nullptr;
+  a.write_partials = 0;
+  return a;
+}
+
+}  // namespace
+
+sink_attn_status sink_attn_decode_partial(const void* q, const void* k_pages, const void* v_pages,
+                                          const int32_t* page_indptr, const int32_t* page_indices,
+                                          const int32_t* kv_len, const float* sinks, int32_t batch,
+                                          int32_t num_qo_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t page_size, int32_t max_kv_len,
+                                          int32_t num_splits, float sm_scale, float* o_parts,
+                                          float* lse_parts, void* stream) {
+  sink_attn_status st = check_decode_common(q, k_pages, v_pages, page_indptr, page_indices, kv_len,
+                                            sinks, batch, num_qo_heads, num_kv_heads, head_dim,
+                                            page_size, max_kv_len, num_splits, sm_scale);
+  if (st != SINK_ATTN_OK) return st;
+  if (!o_parts || !lse_parts)
+    return fail(SINK_ATTN_ERR_NULL_ARG, "decode_partial: o_parts and lse_parts are required");
+  if (!aligned(o_parts, 16) || !aligned(lse_parts, 4))
+    return fail(SINK_ATTN_ERR_MISALIGNED,
+                "decode_partial: o_parts must be 16-byte and lse_parts 4-byte aligned");
+  const int32_t S = plan_splits(batch, num_kv_heads, max_kv_len, num_splits);
+  sa::DecodeArgs a = decode_args(q, k_pages, v_pages, page_indptr, page_indices, kv_len, sinks,
+                                 batch, num_qo_heads, num_kv_heads, max_kv_len, S, sm_scale);
+  a.o_part = o_parts;
+  a.lse_part = lse_parts;
+  a.write_partials = 1;
+  return hip_status(sa::launch_decode(a, num_qo_heads / num_kv_heads,
+                                      static_cast<hipStream_t>(stream)),
+                    "decode_partial launch");
+}
+
+sink_attn_status sink_attn_decode(const void* q, const void* k_pages, const void* v_pages,
+                                  const int32_t* page_indptr, const int32_t* page_indices,
+                                  const int32_t* kv_len, const float* sinks, int32_t batch,
+                                  int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t page_size, int32_t max_kv_len, int32_t num_splits,
+                                  float sm_scale, void* out, sink_attn_dtype out_dtype, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  sink_attn_status st = check_decode_common(q, k_pages, v_pages, page_indptr, page_indices, kv_len,
+                                            sinks, batch, num_qo_heads, num_kv_heads, head_dim,
+                                            page_size, max_kv_len, num_splits, sm_scale);
+  if (st != SINK_ATTN_OK) return st;
+  if (!out) return fail(SINK_ATTN_ERR_NULL_ARG, "decode: out is required");
+  if (out_dtype != SINK_ATTN_BF16 && out_dtype != SINK_ATTN_F32)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "decode: unknown out_dtype %d", (int)out_dtype);
+  if (!aligned(out, 16) || (lse && !aligned(lse, 4)))
+    return fail(SINK_ATTN_ERR_MISALIGNED, "decode: out must be 16-byte and lse 4-byte aligned");
+
+  const int32_t S = plan_splits(batch, num_kv_heads, max_kv_len, num_splits);
+  const size_t need = sink_attn_decode_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim,
+                                                      max_kv_len, num_splits);
+  if (need > 0) {
+    if (!workspace)
+      return fail(SINK_ATTN_ERR_WORKSPACE, "decode: %d splits need a %zu-byte workspace", S, need);
+    if (workspace_bytes < need)
+      return fail(SINK_ATTN_ERR_WORKSPACE, "decode: workspace of %zu bytes < %zu needed",
+                  workspace_bytes, need);
+    if (!aligned(workspace, 16))
+      return fail(SINK_ATTN_ERR_MISALIGNED, "decode: workspace must be 16-byte aligned");
+  }
+
+  sa::DecodeArgs a = decode_args(q, k_pages, v_pages, page_indptr, page_indices, kv_len, sinks,
+                                 batch, num_qo_heads, num_kv_heads, max_kv_len, S, sm_scale);
+  a.out = out;
+  a.out_f32 = out_dtype == SINK_ATTN_F32;
+  a.lse = lse;
+  if (S > 1) {
+    a.o_part = static_cast<float*>(workspace);
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          (size_t)batch * num_qo_heads * S * head_dim * sizeof(float));
+    a.write_partials = 1;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(sa::launch_decode(a, num_qo_heads / num_kv_heads, s), "decode launch");
+  if (st != SINK_ATTN_OK || S == 1) return st;
+
+  sa::MergeArgs m;
+  m.o_parts = a.o_part;
+  m.lse_parts = a.lse_part;
+  m.rows = batch;
+  m.heads = num_qo_heads;
+  m.splits = S;
+  m.out = out;
+  m.out_f32 = a.out_f32;
+  m.lse = lse;
+  return hip_status(sa::launch_merge(m, s), "decode merge launch");
+}
+
+}  // extern "C"

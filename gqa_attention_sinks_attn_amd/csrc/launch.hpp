@@ -1,0 +1,61 @@
+// Internal launch interface between the C ABI layer (api.cpp) and the
+// kernels.  Host code only; every pointer here has been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+struct DecodeArgs {
+  const uint16_t* q;            // bf16 [B, Hq, 64]
+  const uint16_t* k;            // bf16 [num_pages, Hkv, 16, 64]
+  const uint16_t* v;
+  const int32_t* page_indptr;   // [B+1]
+  const int32_t* page_indices;  // [nnz]
+  const int32_t* kv_len;        // [B]
+  const float* sinks;           // [Hq] or nullptr
+  int32_t batch, hq, hkv;
+  int32_t num_splits;           // S >= 1
+  int32_t chunk_pages;          // pages per split
+  float scale_log2;             // sm_scale * log2(e)
+  void* out;                    // final output (S == 1)
+  int32_t out_f32;
+  float* lse;                   // final lse or nullptr (S == 1)
+  float* o_part;                // [B, Hq, S, 64] (S > 1)
+  float* lse_part;              // [B, Hq, S]
+  int32_t write_partials;       // 1: write o_part/lse_part, 0: write out/lse
+};
+
+struct MergeArgs {
+  const float* o_parts;         // [N, H, S, 64]
+  const float* lse_parts;       // [N, H, S] natural log
+  int32_t rows, heads, splits;
+  void* out;
+  int32_t out_f32;
+  float* lse;                   // nullable
+};
+
+struct PrefillArgs {
+  const uint16_t* q;            // bf16 [total_q, Hq, 64]
+  const int32_t* qo_indptr;     // [B+1]
+  const uint16_t* k;            // contiguous [total_kv, Hkv, 64] or paged
+  const uint16_t* v;
+  const int32_t* kv_indptr;     // token offsets or page offsets
+  const int32_t* page_indices;  // nullptr = contiguous
+  const int32_t* kv_len;        // nullptr = kv_indptr gaps (contiguous only)
+  const float* sinks;
+  int32_t batch, hq, hkv;
+  int32_t max_qlen;
+  int32_t causal;
+  float scale_log2;
+  void* out;
+  int32_t out_f32;
+  float* lse;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,226 @@
+/*
+ * sink_attn.h — C ABI of the MI355X (gfx950) sink-attention library.
+ *
+ * The operation (GPT-OSS on Day 0, Perplexity: "Attention: GQA with
+ * attention sinks", and "Sink attention" under "Kernels for GPT-OSS"):
+ * grouped-query attention in which every query head h owns one pretrained
+ * scalar sink sigma_h that takes part in that head's softmax as one extra
+ * logit with no value vector.  For a query row with allowed keys J:
+ *
+ *     M   = max({tau * q.k_j : j in J} U {sigma_h})
+ *     Z   = exp(sigma_h - M) + sum_{j in J} exp(tau * q.k_j - M)
+ *     o   = sum_{j in J} exp(tau * q.k_j - M) / Z * v_j
+ *     lse = M + ln Z                                   (natural log)
+ *
+ * The page computes this online: a running maximum m started at the head's
+ * sink and a running scale d started at 1, so the sink enters the
+ * denominator exactly once; when the key sequence is split into chunks the
+ * sink belongs to the first chunk only (same section).  Query head h reads
+ * KV head h / (Hq / Hkv).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless stated; `stream` is a hipStream_t
+ *     passed as void* (NULL = the null stream).  Work is enqueued on it and
+ *     the call returns without synchronising.  The caller owns every buffer
+ *     and keeps inputs alive until the stream's work completes.
+ *   - The library allocates no device memory, keeps no pointer after
+ *     returning and holds no state other than a thread-local error string,
+ *     so calls from several host threads are safe.
+ *   - bf16 tensors are raw bfloat16 bit patterns; all of q, k, v, out and a
+ *     workspace must be 16-byte aligned; int32 index arrays 4-byte aligned.
+ *   - head_dim must be 64 and page_size 16 (SINK_ATTN_ERR_UNSUPPORTED
+ *     otherwise).  Hq must be a multiple of Hkv; prefill supports
+ *     Hq / Hkv in {1, 2, 4, 8}, decode Hq / Hkv in {1, 2, 4, 8, 16}.
+ *   - sinks: fp32 [Hq] in logit units (not multiplied by sm_scale); NULL
+ *     means no sink (sigma = -inf), i.e. standard attention.  A sink of
+ *     +inf gives o = 0, lse = +inf.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     error return means nothing was launched or written.  Device index
+ *     data (indptr, page ids, lengths) cannot be validated without a
+ *     device->host copy and must be consistent with the host scalars
+ *     (max_qlen, max_kv_len, num_pages) passed alongside.  A launch failure
+ *     reported by the HIP runtime returns SINK_ATTN_ERR_HIP; a fault inside
+ *     a kernel surfaces at the caller's next synchronisation.
+ *   - Empty rows (no allowed key): o = 0, lse = sigma (or -inf).
+ *   - NaN or Inf in q, k or v propagate; nothing scans the inputs.
+ */
+#ifndef SINK_ATTN_H_
+#define SINK_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SINK_ATTN_OK = 0,
+  SINK_ATTN_ERR_NULL_ARG = 1,     /* a required pointer is NULL              */
+  SINK_ATTN_ERR_BAD_SHAPE = 2,    /* non-positive or inconsistent sizes      */
+  SINK_ATTN_ERR_UNSUPPORTED = 3,  /* valid but not built (head_dim, ...)     */
+  SINK_ATTN_ERR_MISALIGNED = 4,   /* a pointer breaks its alignment rule     */
+  SINK_ATTN_ERR_WORKSPACE = 5,    /* workspace missing or too small          */
+  SINK_ATTN_ERR_HIP = 6           /* the HIP runtime reported an error       */
+} sink_attn_status;
+
+typedef enum {
+  SINK_ATTN_BF16 = 0,
+  SINK_ATTN_F32 = 1
+} sink_attn_dtype;
+
+/*
+ * Causal (or full) attention over a ragged batch of query chunks.
+ * Prefill half of the sink-aware attention template (same section: one
+ * template serves prefill and decode).
+ *
+ *   q            bf16 [total_q, Hq, 64]; request b owns query rows
+ *                qo_indptr[b] .. qo_indptr[b+1]-1.
+ *   qo_indptr    int32 [batch+1], non-decreasing, qo_indptr[0] = 0,
+ *                qo_indptr[batch] = total_q.
+ *   k, v         page_indices == NULL: contiguous bf16 [total_kv, Hkv, 64],
+ *                request b owns tokens kv_indptr[b] .. kv_indptr[b+1]-1.
+ *                page_indices != NULL: paged bf16 [num_pages, Hkv, 16, 64]
+ *                (one 2 KiB block per page and KV head); token j of request
+ *                b is slot j % 16 of page page_indices[kv_indptr[b] + j/16].
+ *   kv_indptr    int32 [batch+1]: token offsets (contiguous) or offsets into
+ *                page_indices (paged).
+ *   page_indices int32 [nnz] page ids, or NULL for the contiguous layout.
+ *   kv_len       int32 [batch] keys per request; required when paged, may
+ *                be NULL when contiguous (then kv_indptr[b+1]-kv_indptr[b]).
+ *                Query t of request b sits at absolute position
+ *                kv_len[b] - qlen_b + t (the new tokens are the last qlen_b
+ *                keys) and, when causal, sees keys 0 .. that position.
+ *                Requires qlen_b <= kv_len[b] when causal.
+ *   sinks        fp32 [Hq] or NULL.
+ *   max_qlen     host upper bound of qlen_b (sizes the grid, no device read).
+ *   max_kv_len   host upper bound of kv_len[b].
+ *   sm_scale     tau, multiplies q.k (e.g. 1/sqrt(64)).
+ *   causal       1 = causal, 0 = every query sees all kv_len[b] keys.
+ *   out          [total_q, Hq, 64] in out_dtype (bf16 rounded to nearest
+ *                even, or fp32).
+ *   lse          fp32 [total_q, Hq] natural-log denominators, or NULL.
+ */
+sink_attn_status sink_attn_prefill(
+    const void* q, const int32_t* qo_indptr,
+    const void* k, const void* v, const int32_t* kv_indptr,
+    const int32_t* page_indices, const int32_t* kv_len,
+    const float* sinks,
+    int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t page_size,
+    int32_t total_q, int32_t max_qlen, int32_t max_kv_len,
+    float sm_scale, int32_t causal,
+    void* out, sink_attn_dtype out_dtype, float* lse,
+    void* stream);
+
+/*
+ * Number of KV splits the decode planner uses for these sizes when
+ * num_splits = 0 is passed (always >= 1).  Host-only; no device access.
+ */
+int32_t sink_attn_decode_num_splits(int32_t batch, int32_t num_qo_heads,
+                                    int32_t num_kv_heads, int32_t max_kv_len,
+                                    int32_t num_splits);
+
+/*
+ * Workspace bytes that sink_attn_decode needs for these sizes (0 when the
+ * plan has a single split: then the kernel writes the output directly).
+ * num_splits = 0 means the automatic plan.  Layout inside the workspace:
+ * fp32 partial outputs [batch, Hq, S, 64] followed by fp32 partial
+ * log-sum-exps [batch, Hq, S].
+ */
+size_t sink_attn_decode_workspace_size(int32_t batch, int32_t num_qo_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t max_kv_len, int32_t num_splits);
+
+/*
+ * One query token per request against a paged KV cache, split along the
+ * KV length (same section: work parallelised across heads and along the
+ * KV sequence; the sink enters the first chunk only).
+ *
+ *   q            bf16 [batch, Hq, 64]; the query of request b sits at
+ *                position kv_len[b]-1 and sees all kv_len[b] keys (its own
+ *                key/value are already in the cache).
+ *   k_pages, v_pages, page_indptr, page_indices, kv_len: paged layout as in
+ *                sink_attn_prefill (page_indptr = kv_indptr).
+ *   max_kv_len   host upper bound of kv_len[b].
+ *   num_splits   S >= 1 chunks of ceil(max_kv_len/S) keys rounded up to a
+ *                multiple of 16, or 0 for the automatic plan.  Chunk 0 (keys
+ *                0 ..) carries the sink; a chunk past a request's keys is
+ *                empty.  S > 1 writes partials to the workspace, then merges
+ *                them on the same stream.
+ *   out          [batch, Hq, 64] in out_dtype;  lse fp32 [batch, Hq] or NULL.
+ *   workspace    device buffer of at least sink_attn_decode_workspace_size()
+ *                bytes (may be NULL when that size is 0).
+ */
+sink_attn_status sink_attn_decode(
+    const void* q,
+    const void* k_pages, const void* v_pages,
+    const int32_t* page_indptr, const int32_t* page_indices,
+    const int32_t* kv_len,
+    const float* sinks,
+    int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t page_size,
+    int32_t max_kv_len, int32_t num_splits,
+    float sm_scale,
+    void* out, sink_attn_dtype out_dtype, float* lse,
+    void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/*
+ * The first half of sink_attn_decode on its own: the split-KV partial pass,
+ * without the merge.  Same arguments and planning as sink_attn_decode
+ * (num_splits = 0 -> automatic plan; the plan's S is
+ * sink_attn_decode_num_splits()).  Writes every chunk's partial, also when
+ * S = 1, so that sink_attn_merge(o_parts, lse_parts, batch, Hq, S, ...)
+ * completes the decode:
+ *   o_parts      fp32 [batch, Hq, S, 64]  (each normalised by its own
+ *                denominator; 0 for an empty chunk)
+ *   lse_parts    fp32 [batch, Hq, S]      natural log; -inf for an empty
+ *                chunk, sigma_h for an empty chunk 0 that holds the sink.
+ */
+sink_attn_status sink_attn_decode_partial(
+    const void* q,
+    const void* k_pages, const void* v_pages,
+    const int32_t* page_indptr, const int32_t* page_indices,
+    const int32_t* kv_len,
+    const float* sinks,
+    int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t page_size,
+    int32_t max_kv_len, int32_t num_splits,
+    float sm_scale,
+    float* o_parts, float* lse_parts,
+    void* stream);
+
+/*
+ * Merge of split-KV partials by log-sum-exp: L = max_c lse_c,
+ * w_c = exp(lse_c - L), o = sum w_c o_c / sum w_c, lse = L + ln sum w_c.
+ * Takes no sink: the sink already sits inside chunk 0's partial.
+ *
+ *   o_parts      fp32 [num_rows, num_heads, num_splits, 64], each partial
+ *                normalised by its own denominator.
+ *   lse_parts    fp32 [num_rows, num_heads, num_splits], natural log;
+ *                -inf marks an empty chunk.
+ *   out          [num_rows, num_heads, 64] in out_dtype; lse_out fp32
+ *                [num_rows, num_heads] or NULL.  All chunks empty gives
+ *                o = 0, lse = -inf.
+ */
+sink_attn_status sink_attn_merge(
+    const float* o_parts, const float* lse_parts,
+    int32_t num_rows, int32_t num_heads, int32_t num_splits, int32_t head_dim,
+    void* out, sink_attn_dtype out_dtype, float* lse_out,
+    void* stream);
+
+/* Static description of a status code. */
+const char* sink_attn_status_string(sink_attn_status s);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char* sink_attn_last_error(void);
+
+/* Library version string. */
+const char* sink_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINK_ATTN_H_ */

@@ -1,0 +1,179 @@
+"""C-ABI tests that need no GPU: the library loads, exports every entry point
+that include/sink_attn.h declares, and rejects bad arguments on the host
+before anything is enqueued (so no device is touched).  Fake, aligned
+addresses stand in for device pointers: validation never dereferences."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sink_attn.h")
+
+import gqa_attention_sinks_attn_amd as sa  # noqa: E402
+
+OK, NULL, SHAPE, UNSUP, MISAL, WS, HIP = range(7)
+A = 0x10000    # a 16-byte aligned fake address
+A2 = 0x20000
+A3 = 0x30000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(sink_attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) >= {"sink_attn_prefill", "sink_attn_decode", "sink_attn_merge",
+                          "sink_attn_decode_workspace_size", "sink_attn_status_string",
+                          "sink_attn_last_error"}
+    lib = ctypes.CDLL(sa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(sa.SYMBOLS) == set(names)
+
+
+def test_status_strings():
+    for s in range(7):
+        assert sa.sink_attn_status_string(s)
+    assert sa.sink_attn_status_string(99) == "unknown status"
+    assert "gfx950" in sa.sink_attn_version()
+
+
+def prefill_args(**over):
+    args = dict(q=A, qo_indptr=A, k=A, v=A, kv_indptr=A, page_indices=None, kv_len=None,
+                sinks=A, batch=2, num_qo_heads=64, num_kv_heads=8, head_dim=64, page_size=16,
+                total_q=10, max_qlen=6, max_kv_len=6, sm_scale=0.125, causal=1, out=A2,
+                out_dtype=0, lse=A3, stream=0)
+    args.update(over)
+    return args
+
+
+def call_prefill(**over):
+    a = prefill_args(**over)
+    return sa.lib().sink_attn_prefill(
+        a["q"], a["qo_indptr"], a["k"], a["v"], a["kv_indptr"], a["page_indices"], a["kv_len"],
+        a["sinks"], a["batch"], a["num_qo_heads"], a["num_kv_heads"], a["head_dim"],
+        a["page_size"], a["total_q"], a["max_qlen"], a["max_kv_len"], a["sm_scale"],
+        a["causal"], a["out"], a["out_dtype"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), NULL), (dict(out=None), NULL), (dict(kv_indptr=None), NULL),
+    (dict(page_indices=A, kv_len=None), NULL),
+    (dict(batch=0), SHAPE), (dict(total_q=-1), SHAPE), (dict(max_qlen=11), SHAPE),
+    (dict(num_kv_heads=7), SHAPE), (dict(num_qo_heads=0), SHAPE), (dict(sm_scale=0.0), SHAPE),
+    (dict(sm_scale=float("inf")), SHAPE), (dict(max_kv_len=0), SHAPE),
+    (dict(head_dim=128), UNSUP), (dict(page_indices=A, kv_len=A, page_size=32), UNSUP),
+    (dict(num_qo_heads=128, num_kv_heads=8), UNSUP), (dict(num_qo_heads=24, num_kv_heads=8), UNSUP),
+    (dict(out_dtype=7), UNSUP),
+    (dict(q=A + 2), MISAL), (dict(k=A + 8), MISAL), (dict(out=A2 + 4), MISAL),
+    (dict(qo_indptr=A + 1), MISAL), (dict(lse=A3 + 2), MISAL),
+])
+def test_prefill_rejects(over, code):
+    assert call_prefill(**over) == code
+    assert sa.sink_attn_last_error() != ""
+
+
+def test_prefill_empty_batch_is_a_noop():
+    # nothing to compute -> OK without touching the device
+    assert call_prefill(total_q=0, max_qlen=0) == OK
+    assert sa.sink_attn_last_error() == ""
+
+
+def call_decode(**over):
+    a = dict(q=A, k=A, v=A, page_indptr=A, page_indices=A, kv_len=A, sinks=A, batch=4,
+             num_qo_heads=64, num_kv_heads=8, head_dim=64, page_size=16, max_kv_len=131072,
+             num_splits=32, sm_scale=0.125, out=A2, out_dtype=0, lse=None, workspace=A3,
+             workspace_bytes=0, stream=0)
+    a.update(over)
+    return sa.lib().sink_attn_decode(
+        a["q"], a["k"], a["v"], a["page_indptr"], a["page_indices"], a["kv_len"], a["sinks"],
+        a["batch"], a["num_qo_heads"], a["num_kv_heads"], a["head_dim"], a["page_size"],
+        a["max_kv_len"], a["num_splits"], a["sm_scale"], a["out"], a["out_dtype"], a["lse"],
+        a["workspace"], a["workspace_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), NULL), (dict(page_indices=None), NULL), (dict(kv_len=None), NULL),
+    (dict(batch=-1), SHAPE), (dict(num_splits=-2), SHAPE), (dict(num_kv_heads=3), SHAPE),
+    (dict(head_dim=96), UNSUP), (dict(page_size=8), UNSUP),
+    (dict(num_qo_heads=256, num_kv_heads=8), UNSUP),
+    (dict(v=A + 2), MISAL), (dict(kv_len=A + 2), MISAL),
+    (dict(workspace=None, workspace_bytes=10 ** 9), WS), (dict(workspace_bytes=100), WS),
+])
+def test_decode_rejects(over, code):
+    assert call_decode(**over) == code
+    assert sa.sink_attn_last_error() != ""
+
+
+def call_partial(**over):
+    a = dict(q=A, k=A, v=A, page_indptr=A, page_indices=A, kv_len=A, sinks=None, batch=4,
+             num_qo_heads=64, num_kv_heads=8, head_dim=64, page_size=16, max_kv_len=4096,
+             num_splits=0, sm_scale=0.125, o=A2, l=A3, stream=0)
+    a.update(over)
+    return sa.lib().sink_attn_decode_partial(
+        a["q"], a["k"], a["v"], a["page_indptr"], a["page_indices"], a["kv_len"], a["sinks"],
+        a["batch"], a["num_qo_heads"], a["num_kv_heads"], a["head_dim"], a["page_size"],
+        a["max_kv_len"], a["num_splits"], a["sm_scale"], a["o"], a["l"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(o=None), NULL), (dict(l=None), NULL), (dict(k=None), NULL), (dict(batch=0), SHAPE),
+    (dict(head_dim=32), UNSUP), (dict(o=A2 + 4), MISAL), (dict(l=A3 + 2), MISAL),
+])
+def test_decode_partial_rejects(over, code):
+    assert call_partial(**over) == code
+
+
+def test_decode_rejects_misaligned_workspace():
+    need = sa.sink_attn_decode_workspace_size(4, 64, 8, 64, 131072, 32)
+    assert call_decode(workspace=A3 + 8, workspace_bytes=need) == MISAL
+
+
+def test_workspace_and_plan():
+    # 32 explicit splits: o [4,64,32,64] fp32 + lse [4,64,32] fp32 (256-B padded)
+    need = sa.sink_attn_decode_workspace_size(4, 64, 8, 64, 131072, 32)
+    assert need == 4 * 64 * 32 * 64 * 4 + ((4 * 64 * 32 * 4 + 255) // 256) * 256
+    assert sa.sink_attn_decode_num_splits(4, 64, 8, 131072, 32) == 32
+    # one split needs no workspace
+    assert sa.sink_attn_decode_workspace_size(64, 64, 8, 64, 16, 0) == 0
+    assert sa.sink_attn_decode_num_splits(64, 64, 8, 16, 0) == 1
+    # never more splits than pages
+    assert sa.sink_attn_decode_num_splits(1, 8, 8, 40, 32) == 3
+    # the automatic plan stays within bounds
+    for B, L in [(1, 1), (64, 4096), (4, 131072), (256, 16384), (1, 10 ** 6)]:
+        s = sa.sink_attn_decode_num_splits(B, 64, 8, L, 0)
+        assert 1 <= s <= 256
+        pages = (L + 15) // 16
+        assert s <= max(1, pages)
+
+
+def call_merge(**over):
+    a = dict(o=A, l=A2, rows=4, heads=64, splits=8, d=64, out=A3, dt=0, lse=None, stream=0)
+    a.update(over)
+    return sa.lib().sink_attn_merge(a["o"], a["l"], a["rows"], a["heads"], a["splits"], a["d"],
+                                    a["out"], a["dt"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(o=None), NULL), (dict(out=None), NULL), (dict(splits=0), SHAPE),
+    (dict(heads=0), SHAPE), (dict(rows=-1), SHAPE), (dict(d=32), UNSUP), (dict(dt=3), UNSUP),
+    (dict(o=A + 4), MISAL), (dict(l=A2 + 1), MISAL),
+])
+def test_merge_rejects(over, code):
+    assert call_merge(**over) == code
+
+
+def test_merge_zero_rows_is_a_noop():
+    assert call_merge(rows=0) == OK
+
+
+def test_python_binding_raises_with_detail():
+    with pytest.raises(sa.SinkAttnError) as e:
+        sa.sink_attn_merge(None, A2, 4, 64, 8, 64, A3, 0, None, stream=0)
+    assert e.value.status == NULL and "required" in e.value.detail

@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path against the fp64 oracle on the same seeded bf16
+inputs.  Bar (per output tensor): max-abs <= 1e-2 and relative L2 <= 5e-3;
+the natural-log LSE within 2e-3 where finite and equal where infinite.
+
+Each test names its case; everything calls the library through the C ABI
+(the thin Python binding) exactly as the benchmark does.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+import workloads as W  # noqa: E402
+from tests._helpers import rel_l2  # noqa: E402
+
+MAX_ABS = 1e-2
+REL_L2 = 5e-3
+LSE_ABS = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_attention_sinks_attn_amd  # noqa: F401  (fails loudly if not built)
+    yield
+
+
+def gpu_run(b, out_dtype=None, stream=None):
+    from gqa_attention_sinks_attn_amd import device
+    db = device.to_device(b, out_dtype=out_dtype)
+    device.run(db, stream=stream)
+    torch.cuda.synchronize()
+    return db.out.float().cpu().numpy().astype(np.float64), db.lse.cpu().numpy().astype(np.float64)
+
+
+def check(name, out, ref, lse=None, ref_lse=None):
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert out.shape == ref.shape, name
+    assert np.all(np.isfinite(out)), f"{name}: non-finite output"
+    err = np.abs(out - ref)
+    mx = float(err.max()) if err.size else 0.0
+    rl = rel_l2(out, ref)
+    print(f"[{name}] max_abs={mx:.3e} rel_l2={rl:.3e}", flush=True)
+    assert mx <= MAX_ABS, f"{name}: max abs {mx}"
+    if np.linalg.norm(ref) > 1e-6:
+        assert rl <= REL_L2, f"{name}: rel L2 {rl}"
+    if lse is not None:
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(np.isfinite(lse), fin), f"{name}: lse finiteness"
+        assert np.array_equal(lse[~fin], ref_lse[~fin]), f"{name}: lse infinities"
+        if fin.any():
+            le = float(np.abs(lse[fin] - ref_lse[fin]).max())
+            assert le <= LSE_ABS, f"{name}: lse abs {le}"
+
+
+# ----------------------------------------------------------- the five workloads
+
+def test_c1_tiny_prefill_full():
+    b = W.config(1)
+    out, lse = gpu_run(b)
+    ref, rl = oracle.attend(b)
+    check("c1", out, ref, lse, rl)
+
+
+def test_c2_paged_decode_full():
+    b = W.config(2)
+    out, lse = gpu_run(b)
+    ref, rl = oracle.attend(b)
+    check("c2", out, ref, lse, rl)
+
+
+def test_c3_split_decode_full():
+    b = W.config(3)
+    out, lse = gpu_run(b)
+    ref, rl = oracle.attend(b)
+    check("c3", out, ref, lse, rl)
+
+
+def _sample_rows(b, n, seed):
+    """Sampled (row, head) pairs: every request's first and last token plus
+    uniform draws, over all heads."""
+    rng = np.random.default_rng(seed)
+    rows = [int(b.qo_indptr[i]) for i in range(b.batch)] + \
+           [int(b.qo_indptr[i + 1]) - 1 for i in range(b.batch)]
+    rows += rng.integers(0, b.total_q, size=max(0, n - len(rows))).tolist()
+    rows = np.array(rows, np.int64)
+    heads = rng.integers(0, b.num_qo_heads, size=rows.shape[0]).astype(np.int32)
+    return rows, heads
+
+
+def test_c4_causal_prefill_sampled():
+    b = W.config(4)
+    out, lse = gpu_run(b)
+    rows, heads = _sample_rows(b, 3000, 4)
+    ref, rl = oracle.attend_rows(b, rows, heads)
+    check("c4 sampled", out[rows, heads], ref, lse[rows, heads], rl)
+    # every output row is finite and normalised-sized: |o| <= max |v|
+    assert np.all(np.isfinite(out))
+    assert np.abs(out).max() <= np.abs(W.bf16_bits_to_f32(b.v)).max() + 1e-2
+
+
+def test_c5_mixed_full_size_sampled():
+    mx = W.config(5)
+    for part, n, seed in [(mx.prefill, 3000, 51), (mx.decode, 3000, 52)]:
+        out, lse = gpu_run(part)
+        rows, heads = _sample_rows(part, n, seed)
+        # the planted extreme-sink heads are always in the sample
+        ex = np.array([0, 17, 42, 5, 31, 63], np.int32)
+        rows = np.concatenate([rows, np.repeat(rows[:8], ex.size)])
+        heads = np.concatenate([heads, np.tile(ex, 8)])
+        ref, rl = oracle.attend_rows(part, rows, heads)
+        check(f"c5 {part.kind}", out[rows, heads], ref, lse[rows, heads], rl)
+
+
+# ------------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 33, 100, 4096])
+@pytest.mark.parametrize("splits", [1, 2, 3, 32])
+def test_decode_lengths_and_splits(L, splits):
+    b = W.make_batch(100 + L + splits, kind="decode", qlens=[1, 1, 1], kv_lens=[L, max(1, L // 3), 1],
+                     hq=16, hkv=2, paged=True, sinks="normal", sink_std=2.0, num_splits=splits)
+    out, lse = gpu_run(b)
+    ref, rl = oracle.attend(b)
+    check(f"decode L={L} S={splits}", out, ref, lse, rl)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (16, 4), (64, 8), (32, 2)])
+def test_decode_group_sizes(hq, hkv):
+    b = W.make_batch(7 + hq + hkv, kind="decode", qlens=[1] * 5, kv_lens=[1, 40, 257, 1000, 3],
+                     hq=hq, hkv=hkv, paged=True, sinks="normal", num_splits=0)
+    out, lse = gpu_run(b)
+    ref, rl = oracle.attend(b)
+    check(f"decode G={hq // hkv}", out, ref, lse, rl)
+
+
+@pytest.mark.parametrize("sink", [None, -1e4, 0.0, 10.0, "normal"])
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_sink_values(sink, kind):
+    if kind == "decode":
+        b = W.make_batch(3, kind="decode", qlens=[1] * 4, kv_lens=[5, 64, 300, 1], hq=64, hkv=8,
+                         paged=True, sinks=sink, sink_std=2.0, num_splits=4)
+    else:
+        b = W.make_batch(3, kind="prefill", qlens=[70, 1, 33], kv_lens=[70, 9, 100], hq=64, hkv=8,
+                         paged=True, sinks=sink, sink_std=2.0)
+    out, lse = gpu_run(b)
+    ref, rl = oracle.attend(b)
+    check(f"{kind} sink={sink}", out, ref, lse, rl)
+
+
+def test_infinite_sink():
+    """+inf sink: all mass on the sink, o = 0 and lse = +inf."""
+    s = np.zeros(8, np.float32)
+    s[3] = np.inf
+    for kind in ("decode", "prefill"):
+        b = W.make_batch(5, kind=kind, qlens=[1, 1] if kind == "decode" else [20, 5],
+                         kv_lens=[50, 700], hq=8, hkv=2, paged=True, sinks=s, num_splits=3)
+        out, lse = gpu_run(b)
+        ref, rl = oracle.attend(b)
+        assert np.all(out[:, 3] == 0) and np.all(lse[:, 3] == np.inf)
+        keep = [h for h in range(8) if h != 3]
+        check(f"{kind} +inf sink others", out[:, keep], ref[:, keep], lse[:, keep], rl[:, keep])
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 1), (8, 4), (8, 8), (64, 8), (16, 2)])
+@pytest.mark.parametrize("paged", [False, True])
+def test_prefill_group_sizes_and_layouts(hq, hkv, paged):
+    b = W.make_batch(11 + hq, kind="prefill", qlens=[1, 31, 32, 33, 130], kv_lens=[1, 31, 40, 200, 130],
+                     hq=hq, hkv=hkv, paged=paged, sinks="normal")
+    out, lse = gpu_run(b)
+    ref, rl = oracle.attend(b)
+    check(f"prefill G={hq // hkv} paged={paged}", out, ref, lse, rl)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_chunked_prefix_and_noncausal(causal):
+    b = W.make_batch(21, kind="prefill", qlens=[17, 64, 100], kv_lens=[500, 64, 1000], hq=64, hkv=8,
+                     paged=True, sinks="normal", causal=causal)
+    out, lse = gpu_run(b)
+    ref, rl = oracle.attend(b)
+    check(f"prefill chunked causal={causal}", out, ref, lse, rl)
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_output_dtypes(out_dtype):
+    for kind in ("prefill", "decode"):
+        b = W.make_batch(31, kind=kind, qlens=[40, 7] if kind == "prefill" else [1, 1],
+                         kv_lens=[40, 90], hq=16, hkv=2, paged=True, sinks="normal",
+                         out_dtype=out_dtype, num_splits=2)
+        out, lse = gpu_run(b)
+        ref, rl = oracle.attend(b)
+        check(f"{kind} out={out_dtype}", out, ref, lse, rl)
+
+
+def test_unwritten_cache_slots_do_not_leak():
+    """NaN bit patterns in the unused slots of each last page (never read by
+    the definition) must not reach the output."""
+    b = W.make_batch(41, kind="decode", qlens=[1] * 3, kv_lens=[5, 17, 40], hq=16, hkv=2, paged=True,
+                     sinks="normal", num_splits=2)
+    bp = W.make_batch(41, kind="prefill", qlens=[5, 17, 40], kv_lens=[5, 17, 40], hq=16, hkv=2,
+                      paged=True, sinks="normal")
+    for x in (b, bp):
+        for r, L in enumerate(x.kv_len):
+            last = x.page_indices[x.kv_indptr[r + 1] - 1]
+            used = int(L) % 16
+            if used:
+                x.k[last, :, used:, :] = 0x7FC0  # NaN
+                x.v[last, :, used:, :] = 0x7FC0
+        out, lse = gpu_run(x)
+        ref, rl = oracle.attend(x)
+        check(f"{x.kind} NaN tails", out, ref, lse, rl)
+
+
+def test_merge_against_oracle_partials():
+    """sink_attn_merge on partials the oracle produced, including empty and
+    infinite chunks."""
+    from gqa_attention_sinks_attn_amd import F32, sink_attn_merge
+    b = W.make_batch(61, kind="decode", qlens=[1] * 6, kv_lens=[1, 16, 37, 64, 100, 250], hq=8, hkv=2,
+                     paged=True, sinks="normal", sink_std=2.0)
+    chunk = 32
+    S = (250 + chunk - 1) // chunk
+    parts = [oracle.partial(b, c * chunk, (c + 1) * chunk, include_sink=(c == 0)) for c in range(S)]
+    op = np.stack([p[0] for p in parts], axis=2)
+    lp = np.stack([p[1] for p in parts], axis=2)
+    lp[5, 0, :] = -np.inf       # a row with every chunk empty
+    op[5, 0, :] = 0.0
+    ref, rl = oracle.merge(op, lp)
+    o_t = torch.from_numpy(op.astype(np.float32)).cuda()
+    l_t = torch.from_numpy(lp.astype(np.float32)).cuda()
+    out = torch.empty((6, 8, 64), dtype=torch.float32, device="cuda")
+    lse = torch.empty((6, 8), dtype=torch.float32, device="cuda")
+    sink_attn_merge(o_t, l_t, 6, 8, S, 64, out, F32, lse)
+    torch.cuda.synchronize()
+    check("merge", out.cpu().numpy(), ref, lse.cpu().numpy().astype(np.float64), rl)
+    assert np.all(out.cpu().numpy()[5, 0] == 0) and lse.cpu().numpy()[5, 0] == -np.inf
+
+
+def test_deterministic_and_stream_aware():
+    b = W.make_batch(71, kind="decode", qlens=[1] * 8, kv_lens=[3000] * 8, hq=64, hkv=8, paged=True,
+                     sinks="normal", num_splits=0)
+    from gqa_attention_sinks_attn_amd import device
+    db = device.to_device(b)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        device.run(db)
+        first = db.out.clone()
+        device.run(db)
+    s.synchronize()
+    assert torch.equal(first, db.out)
+    ref, rl = oracle.attend(b)
+    check("decode side stream", db.out.float().cpu().numpy(), ref, db.lse.cpu().numpy(), rl)

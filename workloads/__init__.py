@@ -9,7 +9,10 @@ Recipe (every workload):
   * draw order: (1) lengths, (2) page permutation, (3) Q, (4) K, (5) V,
     (6) sinks;
   * Q, K and V are drawn fp32 ~ N(0, 1), then rounded once to bf16
-    (round-to-nearest-even) on the host; both sides read those bits;
+    (round-to-nearest-even) on the host; both sides read those bits.  Large
+    pools are drawn in chunks of 2^22 values, chunk i from child i of a
+    seed sequence whose seed the workload's generator draws (deterministic
+    for any thread count);
   * a paged cache holds exactly sum(ceil(L_b / page_size)) pages whose ids
     are a random permutation of the pool, handed out in request order, so
     the pages of different requests interleave in memory;
@@ -26,8 +29,10 @@ Layouts (the library's documented format):
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Optional, Sequence
 
 import numpy as np
@@ -118,13 +123,29 @@ def _draw_qkv_pool(rng, shape_q, shape_kv):
     return q, k, v
 
 
-def _normal_bf16(rng, shape, chunk_elems: int = 1 << 26) -> np.ndarray:
-    """N(0,1) fp32 draws rounded to bf16, generated in chunks to bound memory."""
+def _normal_bf16(rng, shape, chunk_elems: int = 1 << 22) -> np.ndarray:
+    """N(0,1) fp32 draws rounded to bf16.  The parent generator draws one
+    128-bit seed; chunk i of 2^22 elements is drawn by child i of that seed
+    sequence, so the values do not depend on how many threads fill them."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, chunk_elems):
+    ss = np.random.SeedSequence(int(rng.integers(0, 2**63)))
+    n_chunks = (n + chunk_elems - 1) // chunk_elems
+    children = ss.spawn(max(n_chunks, 1))
+
+    def fill(i):
+        s = i * chunk_elems
         e = min(n, s + chunk_elems)
-        out[s:e] = to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+        g = np.random.default_rng(children[i])
+        out[s:e] = to_bf16_bits(g.standard_normal(e - s, dtype=np.float32))
+
+    if n_chunks <= 1:
+        if n:
+            fill(0)
+    else:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, range(n_chunks)))
     return out.reshape(shape)
 
 
