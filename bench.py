@@ -4,14 +4,15 @@
 Default workload: paged decode, batch 64, KV lengths uniform in [1, 4096],
 64 query / 8 KV heads, head_dim 64, 16-token pages with a permuted page table
 (the decode workload the headline metric is quoted on).  One step = one
-pass of the decode path: the split-KV partial kernel
-(sink_attn_decode_partial) followed by the LSE merge (sink_attn_merge), both
-through the C ABI.  Metric: KV bytes read per second (2 * Hkv * 64 * 2 B per
-KV token) over the whole step.
+pass of the decode path with the library's automatic split plan: the
+split-KV partial kernel (sink_attn_decode_partial) followed by the LSE merge
+(sink_attn_merge), both through the C ABI.  Metric: KV bytes read per second
+(2 * Hkv * 64 * 2 B per KV token) over the whole step.
 
 Also reported, on the same JSON line:
   * "roofline": the dominant kernel (decode partial) -- algorithmic bytes
-    per launch / its mean launch time from HIP events on its own stream,
+    per launch / its mean launch time from HIP events around it on its own
+    stream,
     against the 8 TB/s HBM peak; "traffic" from rocprofv3 counters when a
     measurement for the current kernel exists, else null;
   * "prefill": the causal prefill workload (8 x 4096 tokens, 64/8 heads,
@@ -20,6 +21,12 @@ Also reported, on the same JSON line:
     decode batch.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --mode traffic   # kernels only, for rocprofv3 --pmc passes
+
+--mode traffic runs, untimed: a plain 256 MiB device-to-device copy three
+times (the calibration dispatch for FETCH_SIZE / WRITE_SIZE), then the decode
+partial kernel eight times on the decode workload (rotating the same four KV
+copies as the timed run), then the prefill kernel three times.
 """
 from __future__ import annotations
 
@@ -38,9 +45,12 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 KV_COPIES = 4                  # rotated KV pools: 4 x 269 MB > 256 MB last-level cache
 
-# HBM bytes per dispatch measured with rocprofv3 counters for the current
-# decode-partial kernel on this workload (None until measured).
-DECODE_TRAFFIC_BYTES = None
+# HBM bytes per dispatch from rocprofv3 FETCH_SIZE + WRITE_SIZE passes
+# (python bench.py --mode traffic), each scaled by the same counter on a
+# 256 MiB copy; see profiles/.  Valid for the kernel sources they were taken
+# on -- reset to None whenever decode.hip or prefill.hip changes.
+DECODE_TRAFFIC_BYTES = 262_838_247
+PREFILL_TRAFFIC_BYTES = 1_362_741_767
 
 
 def log(msg: str):
@@ -73,6 +83,7 @@ def bench_decode(args, torch, sa, device, W):
     B, Hq, D = db.batch, db.num_qo_heads, db.head_dim
     o_parts = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
     lse_parts = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    out_code = sa.F32 if db.out.dtype == torch.float32 else sa.BF16
     ks = [db.k] + [db.k.clone() for _ in range(KV_COPIES - 1)]
     vs = [db.v] + [db.v.clone() for _ in range(KV_COPIES - 1)]
     torch.cuda.synchronize()
@@ -86,7 +97,7 @@ def bench_decode(args, torch, sa, device, W):
                                     db.num_splits, db.sm_scale, o_parts, lse_parts)
         if ev is not None:
             ev[1].record()
-        sa.sink_attn_merge(o_parts, lse_parts, B, Hq, S, D, db.out, sa.BF16, db.lse)
+        sa.sink_attn_merge(o_parts, lse_parts, B, Hq, S, D, db.out, out_code, db.lse)
 
     for i in range(args.warmup):
         step(i)
@@ -133,7 +144,7 @@ def bench_prefill(args, torch, sa, device, W):
                 ms_per_call=round(ms, 4), flop_per_call=flops, steps=steps,
                 roofline=dict(bound="mfma", achieved=round(tfs, 2), peak=BF16_PEAK_TFLOPS,
                               unit="TFLOP/s", frac=round(tfs / BF16_PEAK_TFLOPS, 4),
-                              traffic=None))
+                              traffic=PREFILL_TRAFFIC_BYTES))
 
 
 def cpu_baseline(b, kv_bytes, seconds):
@@ -153,6 +164,37 @@ def cpu_baseline(b, kv_bytes, seconds):
                        f"all 64 heads), fp64, {len(times)} run(s), mean {mean:.3f} s")
 
 
+def traffic_run(torch, sa, device, W):
+    """Untimed dispatches for hardware-counter passes (see module doc)."""
+    x = torch.ones(256 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"[traffic] copy: {x.numel() * 4} bytes read and written per dispatch")
+    b = W.config(2)
+    db = device.to_device(b)
+    S = device.splits_of(db)
+    B, Hq, D = db.batch, db.num_qo_heads, db.head_dim
+    op = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
+    lp = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    ks = [db.k] + [db.k.clone() for _ in range(KV_COPIES - 1)]
+    vs = [db.v] + [db.v.clone() for _ in range(KV_COPIES - 1)]
+    for i in range(8):
+        sa.sink_attn_decode_partial(db.q, ks[i % KV_COPIES], vs[i % KV_COPIES], db.kv_indptr,
+                                    db.page_indices, db.kv_len, db.sinks, B, Hq, db.num_kv_heads,
+                                    D, db.page_size, db.max_kv_len, db.num_splits, db.sm_scale,
+                                    op, lp)
+    torch.cuda.synchronize()
+    log(f"[traffic] decode partial: {decode_algorithmic_bytes(b)} algorithmic bytes per dispatch")
+    pb = W.config(4)
+    pdb = device.to_device(pb, with_lse=False)
+    for _ in range(3):
+        device.run(pdb)
+    torch.cuda.synchronize()
+    log(f"[traffic] prefill: {prefill_pairs(pb) * 4 * pb.head_dim} flop per dispatch")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +203,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--mode", choices=["bench", "traffic"], default="bench")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus "
@@ -175,6 +218,10 @@ def main():
     import gqa_attention_sinks_attn_amd as sa
     from gqa_attention_sinks_attn_amd import device
     import workloads as W
+
+    if args.mode == "traffic":
+        traffic_run(torch, sa, device, W)
+        return
 
     log("[bench] decode workload: generating inputs")
     dec = bench_decode(args, torch, sa, device, W)
@@ -208,7 +255,7 @@ def main():
             "workload": W.CONFIG_NAMES[2],
             "batch": b.batch, "kv_tokens": int(b.kv_len.sum()), "num_qo_heads": b.num_qo_heads,
             "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "page_size": b.page_size,
-            "num_splits": dec["S"], "kv_copies_rotated": KV_COPIES,
+            "num_splits": dec["S"], "kv_copies_rotated": KV_COPIES, "out_dtype": "f32",
             "step": "sink_attn_decode_partial + sink_attn_merge",
         },
         "roofline": {

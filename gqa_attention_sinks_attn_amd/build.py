@@ -34,6 +34,9 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-result",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # device code only: no NaN canonicalisation around fmaxf (IEEE
+           # mode off); the kernels never depend on NaN semantics
+           "-Xarch_device", "-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee",
            "-I", INCLUDE, "-I", CSRC]
     cmd += list(extra_flags or [])
     cmd += [os.path.join(CSRC, s) for s in SOURCES]

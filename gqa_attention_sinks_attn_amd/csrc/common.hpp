@@ -58,6 +58,27 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
+// lane j receives element j % 4 of the 8-byte words that lanes 4 e + j / 4
+// of the group point at, for e = 0..3.  So if lane s points at row
+// (r0 + s / 4), columns (c0 + 4 (s % 4)) of a row-major bf16 matrix, lane
+// j receives column c0 + j of rows r0 .. r0 + 3: a 4 x 16 block transposed.
+__device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Two transposed reads forming one 8-value MFMA operand (slots 0-3 from
+// `lo`, slots 4-7 from `hi`).
+__device__ __forceinline__ u32x4 lds_tr16_pair(const uint16_t* lo, const uint16_t* hi) {
+  const u32x2 a = lds_tr16(lo);
+  const u32x2 b = lds_tr16(hi);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 // Cross-lane exchange with lane ^ mask (mask in {16, 32}) through
 // ds_bpermute; wave-uniform control flow required.
 __device__ __forceinline__ float xor_lane(float v, int mask) {

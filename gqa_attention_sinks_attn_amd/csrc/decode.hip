@@ -7,19 +7,22 @@
 // first chunk may carry it.  Work is parallel over heads and along the KV
 // length (same passage).
 //
-// One workgroup = (request b, KV head g, chunk c).  Its four waves take the
-// chunk's pages two at a time, round robin, each wave keeping its own online
-// state for the G query heads of KV head g; the four states are merged in
-// LDS at the end.  Per two-page step a wave:
-//   * gathers the two page ids (scalar loads) and loads K straight into
-//     MFMA operand registers (16 B per lane per load),
-//   * stages V (2 x 2 KiB) in a wave-private LDS slice,
+// One workgroup = (request b, KV head g, chunk c); the grid lists every
+// chunk-0 workgroup first.  Its four waves take the chunk's pages two at a
+// time, round robin, each keeping its own online state for the G query heads
+// of KV head g; the four states are merged in LDS at the end.  Per two-page
+// step a wave:
+//   * takes the two page ids from a register that holds the ids of its next
+//     32 steps (one vector load per 32 steps, read back with readlane),
+//   * has already issued the step's K and V loads one step earlier (software
+//     pipeline, two register sets in flight per wave),
 //   * computes S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (16 keys x 16 head
-//     columns; columns >= G are padding),
+//     columns; columns >= G are padding) with K straight from registers,
 //   * updates m, d and O in the exp2 domain, and
-//   * accumulates O^T += V^T P^T on the same MFMA, with P^T taken straight
-//     from the score registers (the key order inside the contraction is the
-//     one the score layout gives, and V^T is read from LDS to match).
+//   * accumulates O^T += V^T P^T on the same MFMA.  P^T comes straight from
+//     the score registers; V is staged in a wave-private LDS slice in its
+//     natural [key][dim] layout and read back transposed with
+//     ds_read_b64_tr_b16 in the key order the score layout produces.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -29,9 +32,8 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kPage = 16;
 constexpr int kD = 64;
-constexpr int kRowElems = 68;            // LDS row stride in bf16 (136 B)
-constexpr int kStepRows = 2 * kPage;     // rows of V staged per wave-step
-constexpr int kWaveLds = kStepRows * kRowElems;   // bf16 elements per wave
+constexpr int kVPitch = 80;                      // LDS row pitch in bf16 (160 B)
+constexpr int kWaveLds = 2 * kPage * kVPitch;    // bf16 elements per wave slice
 
 struct alignas(16) CombineSlot {
   float m[16];
@@ -44,14 +46,20 @@ constexpr int kLdsBytes =
         ? (kWaves * kWaveLds * 2)
         : (kWaves * (int)sizeof(CombineSlot));
 
+struct StepRegs {
+  u32x4 k00, k01, k10, k11;   // K: page 0/1, dims 8 grp + {0, 32}
+  u32x4 v00, v01, v10, v11;   // V: page 0/1, 32 contiguous bytes each
+};
+
 template <int G>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kLdsBytes];
   uint16_t* lds_v = reinterpret_cast<uint16_t*>(lds_raw);
 
-  const int c = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  const int unit = blockIdx.x;          // b * Hkv + g
+  const int c = blockIdx.y;             // chunk
+  const int g = unit % p.hkv;
+  const int b = unit / p.hkv;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;     // head column of the MFMA tile
@@ -66,12 +74,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
   const int32_t* pages = p.page_indices + p.page_indptr[b];
 
   // Q^T operand: column `col` = head h, k-step s covers dims 32 s + 8 grp .. +7.
-  bf16x8 bq[2];
+  bf16x8 bq0, bq1;
   {
     const uint16_t* qh = p.q + ((int64_t)b * p.hq + h) * kD + 8 * grp;
-    u32x4 z = {0u, 0u, 0u, 0u};
-    bq[0] = as_bf16x8(live_col ? ld16(qh) : z);
-    bq[1] = as_bf16x8(live_col ? ld16(qh + 32) : z);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    bq0 = as_bf16x8(live_col ? ld16(qh) : z);
+    bq1 = as_bf16x8(live_col ? ld16(qh + 32) : z);
   }
 
   // Online state in log2 units.  The sink-carrying state (wave 0 of chunk
@@ -83,59 +91,67 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
     m = s * kLog2e;
     d = (grp == 0 && s != -INFINITY) ? 1.f : 0.f;
   }
-  f32x4 o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, o2 = o0, o3 = o0;
 
   uint16_t* my_v = lds_v + wave * kWaveLds;
   const int64_t head_stride = (int64_t)kPage * kD;           // one page x head block
   const int64_t page_stride = (int64_t)p.hkv * head_stride;
+  const int koff = col * kD + 8 * grp;                       // K operand offset
+  const int voff = (lane >> 2) * kD + 16 * (lane & 3);       // V: 32 B per lane
 
-  for (int pp = pg0 + 2 * wave; pp < pg1; pp += 2 * kWaves) {
+  // Page ids of this wave's next 32 steps: lane l holds step l / 2, page l % 2.
+  const int first = pg0 + 2 * wave;
+  int ids = 0;
+  auto load_ids = [&](int step0) {
+    const int idx = first + 8 * (step0 + (lane >> 1)) + (lane & 1);
+    ids = idx < pg1 ? pages[idx] : 0;
+  };
+
+  auto issue = [&](StepRegs& r, int step) {
+    const int slot = 2 * (step & 31);
+    const int pp = first + 8 * step;
     const bool two = (pp + 1) < pg1;
-    const int pid0 = pages[pp];
-    const int pid1 = two ? pages[pp + 1] : pid0;
+    const int pid0 = __builtin_amdgcn_readlane(ids, slot);
+    const int pid1 = two ? __builtin_amdgcn_readlane(ids, slot + 1) : pid0;
     const uint16_t* kb0 = p.k + pid0 * page_stride + g * head_stride;
-    const uint16_t* kb1 = p.k + pid1 * page_stride + g * head_stride;
     const uint16_t* vb0 = p.v + pid0 * page_stride + g * head_stride;
+    const uint16_t* kb1 = p.k + pid1 * page_stride + g * head_stride;
     const uint16_t* vb1 = p.v + pid1 * page_stride + g * head_stride;
+    r.k00 = ld16(kb0 + koff);
+    r.k01 = ld16(kb0 + koff + 32);
+    r.k10 = ld16(kb1 + koff);
+    r.k11 = ld16(kb1 + koff + 32);
+    r.v00 = ld16(vb0 + voff);
+    r.v01 = ld16(vb0 + voff + 8);
+    r.v10 = ld16(vb1 + voff);
+    r.v11 = ld16(vb1 + voff + 8);
+  };
 
-    // K operand: row = key (lane % 16), dims 32 s + 8 grp .. +7
-    const int koff = col * kD + 8 * grp;
-    u32x4 k00 = ld16(kb0 + koff), k01 = ld16(kb0 + koff + 32);
-    u32x4 k10 = ld16(kb1 + koff), k11 = ld16(kb1 + koff + 32);
-    // V rows: lane reads 32 contiguous bytes, key lane/4, dims 16 (lane%4) ..
-    const int voff = (lane >> 2) * kD + 16 * (lane & 3);
-    u32x4 v00 = ld16(vb0 + voff), v01 = ld16(vb0 + voff + 8);
-    u32x4 v10 = ld16(vb1 + voff), v11 = ld16(vb1 + voff + 8);
-
+  auto process = [&](StepRegs& r, int step) {
+    const int pp = first + 8 * step;
+    const bool two = (pp + 1) < pg1;
     // Rows past the request's last key (the tail of its last page, or a
-    // missing second page) are zeroed: their probabilities are 0, and 0 times
-    // whatever an unwritten cache slot holds must stay 0 in the MFMA.
+    // missing second page) are zeroed: their probabilities are 0, and 0
+    // times whatever an unwritten cache slot holds must stay 0 in the MFMA.
     {
       const int vkey = pp * kPage + (lane >> 2);
       const u32x4 z = {0u, 0u, 0u, 0u};
-      if (vkey >= L) { v00 = z; v01 = z; }
-      if (!two || vkey + kPage >= L) { v10 = z; v11 = z; }
-    }
-    // stage V in LDS, rows [page*16 + key], 136-byte stride
-    {
-      uint16_t* r0 = my_v + (lane >> 2) * kRowElems + 16 * (lane & 3);
-      uint16_t* r1 = r0 + kPage * kRowElems;
-      u32x2* w0 = reinterpret_cast<u32x2*>(r0);
-      u32x2* w1 = reinterpret_cast<u32x2*>(r1);
-      w0[0] = u32x2{v00[0], v00[1]}; w0[1] = u32x2{v00[2], v00[3]};
-      w0[2] = u32x2{v01[0], v01[1]}; w0[3] = u32x2{v01[2], v01[3]};
-      w1[0] = u32x2{v10[0], v10[1]}; w1[1] = u32x2{v10[2], v10[3]};
-      w1[2] = u32x2{v11[0], v11[1]}; w1[3] = u32x2{v11[2], v11[3]};
+      if (vkey >= L) { r.v00 = z; r.v01 = z; }
+      if (!two || vkey + kPage >= L) { r.v10 = z; r.v11 = z; }
+      uint16_t* r0 = my_v + (lane >> 2) * kVPitch + 16 * (lane & 3);
+      uint16_t* r1 = r0 + kPage * kVPitch;
+      *reinterpret_cast<u32x4*>(r0) = r.v00;
+      *reinterpret_cast<u32x4*>(r0 + 8) = r.v01;
+      *reinterpret_cast<u32x4*>(r1) = r.v10;
+      *reinterpret_cast<u32x4*>(r1 + 8) = r.v11;
     }
 
     // S^T = K Q^T for both pages: lane holds head col, keys 4 grp + i
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    s0 = mfma16(as_bf16x8(k00), bq[0], s0);
-    s0 = mfma16(as_bf16x8(k01), bq[1], s0);
-    s1 = mfma16(as_bf16x8(k10), bq[0], s1);
-    s1 = mfma16(as_bf16x8(k11), bq[1], s1);
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    s0 = mfma16(as_bf16x8(r.k00), bq0, s0);
+    s1 = mfma16(as_bf16x8(r.k10), bq0, s1);
+    s0 = mfma16(as_bf16x8(r.k01), bq1, s0);
+    s1 = mfma16(as_bf16x8(r.k11), bq1, s1);
 
     float sc[8];
     const int key_base = pp * kPage + 4 * grp;
@@ -144,9 +160,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
       sc[i] = (key_base + i < L) ? s0[i] * p.scale_log2 : -INFINITY;
       sc[4 + i] = (two && key_base + kPage + i < L) ? s1[i] * p.scale_log2 : -INFINITY;
     }
-    float mx = sc[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     mx = fmaxf(mx, xor_lane(mx, 16));
     mx = fmaxf(mx, xor_lane(mx, 32));
     const float m_new = fmaxf(m, mx);
@@ -161,26 +176,42 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
     }
     d = d * alpha + psum;
     m = m_new;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    o0 *= alpha; o1 *= alpha; o2 *= alpha; o3 *= alpha;
 
     // P^T operand: slot j <-> key (j < 4 ? 4 grp + j : 16 + 4 grp + j - 4)
-    u32x4 pw = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+    const u32x4 pw = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                      pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
     const bf16x8 pb = as_bf16x8(pw);
 
-    // V^T operand per 16-dim block: row = dim 16 db + col, same key slots
-    const uint16_t* rA = my_v + (4 * grp) * kRowElems + col;
-    const uint16_t* rB = rA + kPage * kRowElems;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int dc = 16 * db;
-      u32x4 vw;
-      vw[0] = (uint32_t)rA[0 * kRowElems + dc] | ((uint32_t)rA[1 * kRowElems + dc] << 16);
-      vw[1] = (uint32_t)rA[2 * kRowElems + dc] | ((uint32_t)rA[3 * kRowElems + dc] << 16);
-      vw[2] = (uint32_t)rB[0 * kRowElems + dc] | ((uint32_t)rB[1 * kRowElems + dc] << 16);
-      vw[3] = (uint32_t)rB[2 * kRowElems + dc] | ((uint32_t)rB[3 * kRowElems + dc] << 16);
-      o[db] = mfma16(as_bf16x8(vw), pb, o[db]);
+    // V^T operand per 16-dim block: row = dim 16 db + col, same key slots.
+    // Source lane s of group grp points at key 4 grp + s / 4, dims
+    // 16 db + 4 (s % 4); lane j then holds V[4 grp + e][16 db + j], e = 0..3.
+    const uint16_t* src = my_v + (4 * grp + (col >> 2)) * kVPitch + 4 * (col & 3);
+    o0 = mfma16(as_bf16x8(lds_tr16_pair(src, src + kPage * kVPitch)), pb, o0);
+    o1 = mfma16(as_bf16x8(lds_tr16_pair(src + 16, src + kPage * kVPitch + 16)), pb, o1);
+    o2 = mfma16(as_bf16x8(lds_tr16_pair(src + 32, src + kPage * kVPitch + 32)), pb, o2);
+    o3 = mfma16(as_bf16x8(lds_tr16_pair(src + 48, src + kPage * kVPitch + 48)), pb, o3);
+  };
+
+  const int n_steps = pg1 > first ? (pg1 - first + 7) / 8 : 0;
+  if (n_steps > 0) {
+    load_ids(0);
+    StepRegs ra, rb;
+    issue(ra, 0);
+    int step = 0;
+    while (true) {
+      if (step + 1 < n_steps) {
+        if (((step + 1) & 31) == 0) load_ids(step + 1);
+        issue(rb, step + 1);
+      }
+      process(ra, step);
+      if (++step >= n_steps) break;
+      if (step + 1 < n_steps) {
+        if (((step + 1) & 31) == 0) load_ids(step + 1);
+        issue(ra, step + 1);
+      }
+      process(rb, step);
+      if (++step >= n_steps) break;
     }
   }
 
@@ -195,11 +226,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
     mine.m[col] = m;
     mine.d[col] = d;
   }
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    float* dst = &mine.o[col][16 * db + 4 * grp];
-    *reinterpret_cast<f32x4*>(dst) = o[db];
-  }
+  *reinterpret_cast<f32x4*>(&mine.o[col][0 + 4 * grp]) = o0;
+  *reinterpret_cast<f32x4*>(&mine.o[col][16 + 4 * grp]) = o1;
+  *reinterpret_cast<f32x4*>(&mine.o[col][32 + 4 * grp]) = o2;
+  *reinterpret_cast<f32x4*>(&mine.o[col][48 + 4 * grp]) = o3;
   __syncthreads();
 
   // 256 threads: column t / 16, dims 4 (t % 16) .. +3
@@ -245,7 +275,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream) {
-  dim3 grid(a.num_splits, a.hkv, a.batch);
+  dim3 grid(a.batch * a.hkv, a.num_splits);
   dim3 block(256);
   switch (group) {
     case 1: hipLaunchKernelGGL(decode_kernel<1>, grid, block, 0, stream, a); break;

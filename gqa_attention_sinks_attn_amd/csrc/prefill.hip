@@ -17,9 +17,19 @@
 //   * each wave computes S^T = K Q^T for its 2 x 32 rows on
 //     v_mfma_f32_32x32x16_bf16, so a lane holds 32 scores of one query row
 //     and the row maximum needs one cross-lane exchange;
-//   * P is rounded to bf16 in registers and fed directly as the B operand
-//     of O^T += V^T P^T; V is stored transposed in LDS in the key order the
-//     score layout produces;
+//   * the running maximum is a reference value m: scores are exponentiated
+//     as exp2(s * scale - m) with one FMA and no per-tile maximum; only when
+//     a row's tile sum would exceed 2^15 (a new, much larger maximum) or the
+//     row has no reference yet does the tile take the slow path that finds
+//     the true maximum and rescales m, d and O -- the same quantity as the
+//     textbook update, with the max reduction and the rescale of O skipped
+//     on almost every tile;
+//   * P is rounded to bf16 in registers and fed directly as the B operand of
+//     O^T += V^T P^T; the row sum d adds exactly those rounded values, so the
+//     weights of every row sum to one; V stays in its natural layout in LDS
+//     and is read
+//     transposed with ds_read_b64_tr_b16 in the key order of the score
+//     layout;
 //   * masking (causal edge, ragged tail) is applied only on tiles that
 //     straddle an edge; late query tiles are launched first.
 #include "common.hpp"
@@ -29,22 +39,16 @@ namespace sa {
 namespace {
 
 constexpr int kD = 64;
-constexpr int kTile = 64;          // keys per tile
-constexpr int kKRow = 72;          // K tile row stride in bf16 (144 B)
-constexpr int kVRow = 68;          // V^T tile row stride in bf16 (136 B)
-constexpr int kKBuf = kTile * kKRow;   // bf16 elements per K buffer
-constexpr int kVBuf = kD * kVRow;      // bf16 elements per V^T buffer
-
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
+constexpr int kTile = 64;            // keys per tile
+constexpr int kKPitch = 72;          // K tile row pitch in bf16 (144 B)
+constexpr int kVPitch = 80;          // V tile row pitch in bf16 (160 B)
+constexpr int kKBuf = kTile * kKPitch;
+constexpr int kVBuf = kTile * kVPitch;
+constexpr float kFastLimit = 32768.f; // lane-partial tile sum that forces a rescale
 
 template <bool PAGED>
 __device__ __forceinline__ const uint16_t* kv_row(const PrefillArgs& p, const uint16_t* base,
-                                                  int b, int g, int key, int kv_start) {
+                                                  int g, int key, int kv_start) {
   if constexpr (PAGED) {
     const int page = p.page_indices[kv_start + (key >> 4)];
     return base + (((int64_t)page * p.hkv + g) * 16 + (key & 15)) * kD;
@@ -53,8 +57,14 @@ __device__ __forceinline__ const uint16_t* kv_row(const PrefillArgs& p, const ui
   }
 }
 
+// acc + lo(w) + hi(w) for a packed bf16 pair, accumulated in fp32.
+__device__ __forceinline__ float dot2_sum(uint32_t w, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
 template <int G, bool PAGED>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs p) {
   constexpr int T = 256 / G;  // tokens per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * kKBuf];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * kVBuf];
@@ -124,7 +134,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs p) {
       for (int j = 0; j < 16; ++j) o[cb][db][j] = 0.f;
   }
 
-  // ---- tile loader: thread -> two K rows (16 B chunk) and a V key pair ----
+  // ---- tile loader: thread -> rows ld_row and 32 + ld_row, one 16 B chunk ----
   const int ld_row = tid >> 3;   // 0..31
   const int ld_chunk = tid & 7;  // 16-byte chunk within a 128-byte row
   u32x4 rk0, rk1, rv0, rv1;
@@ -132,25 +142,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs p) {
     const int key0 = kt * kTile;
     const u32x4 z = {0u, 0u, 0u, 0u};
     const int ka = key0 + ld_row, kb2 = key0 + 32 + ld_row;
-    const int va = key0 + 2 * ld_row, vb = va + 1;
-    rk0 = ka < L ? ld16(kv_row<PAGED>(p, p.k, b, g, ka, kv_start) + 8 * ld_chunk) : z;
-    rk1 = kb2 < L ? ld16(kv_row<PAGED>(p, p.k, b, g, kb2, kv_start) + 8 * ld_chunk) : z;
-    rv0 = va < L ? ld16(kv_row<PAGED>(p, p.v, b, g, va, kv_start) + 8 * ld_chunk) : z;
-    rv1 = vb < L ? ld16(kv_row<PAGED>(p, p.v, b, g, vb, kv_start) + 8 * ld_chunk) : z;
+    const uint16_t* pa = kv_row<PAGED>(p, p.k, g, ka < L ? ka : 0, kv_start) + 8 * ld_chunk;
+    const uint16_t* pb = kv_row<PAGED>(p, p.k, g, kb2 < L ? kb2 : 0, kv_start) + 8 * ld_chunk;
+    const int64_t vdelta = p.v - p.k;
+    rk0 = ka < L ? ld16(pa) : z;
+    rk1 = kb2 < L ? ld16(pb) : z;
+    // V rows past the last key are zero (their weight is 0; 0 x garbage must stay 0)
+    rv0 = ka < L ? ld16(pa + vdelta) : z;
+    rv1 = kb2 < L ? ld16(pb + vdelta) : z;
   };
   auto store_tile = [&](int buf) {
     uint16_t* kd = lds_k + buf * kKBuf;
-    *reinterpret_cast<u32x4*>(kd + ld_row * kKRow + 8 * ld_chunk) = rk0;
-    *reinterpret_cast<u32x4*>(kd + (32 + ld_row) * kKRow + 8 * ld_chunk) = rk1;
-    // V^T: row = dim, column = key; pack the key pair per dim
-    uint32_t* vd = reinterpret_cast<uint32_t*>(lds_v + buf * kVBuf + (8 * ld_chunk) * kVRow +
-                                               2 * ld_row);
-    constexpr int kVRowW = kVRow / 2;  // row stride in 32-bit words
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      vd[(2 * w) * kVRowW] = lo_pair(rv0[w], rv1[w]);
-      vd[(2 * w + 1) * kVRowW] = hi_pair(rv0[w], rv1[w]);
-    }
+    uint16_t* vd = lds_v + buf * kVBuf;
+    *reinterpret_cast<u32x4*>(kd + ld_row * kKPitch + 8 * ld_chunk) = rk0;
+    *reinterpret_cast<u32x4*>(kd + (32 + ld_row) * kKPitch + 8 * ld_chunk) = rk1;
+    *reinterpret_cast<u32x4*>(vd + ld_row * kVPitch + 8 * ld_chunk) = rv0;
+    *reinterpret_cast<u32x4*>(vd + (32 + ld_row) * kVPitch + 8 * ld_chunk) = rv1;
   };
 
   if (n_tiles > 0) {
@@ -160,6 +167,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs p) {
   __syncthreads();
 
   const float sl2 = p.scale_log2;
+  // transposed V reads: 16-lane group q = lane / 16 covers dims 16 (q % 2) ..
+  // of a 32-dim block and keys 4 hh + s / 4 (s = lane % 16)
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < n_tiles) load_tile(kt + 1);
@@ -170,85 +182,110 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs p) {
       const uint16_t* vbuf = lds_v + buf * kVBuf;
       // S^T[kb][cb]: keys 32 kb + 8 (j/4) + 4 hh + j%4, column = row r of cb
       f32x16 sacc[2][2];
+      const f32x16 zero16 = {};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) sacc[kb][cb][j] = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 a = as_bf16x8(
-              *reinterpret_cast<const u32x4*>(kbuf + (32 * kb + r) * kKRow + 16 * s + 8 * hh));
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) sacc[kb][cb] = mfma32(a, bq[cb][s], sacc[kb][cb]);
-        }
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 a0 = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(kbuf + r * kKPitch + 16 * s + 8 * hh));
+        const bf16x8 a1 = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(kbuf + (32 + r) * kKPitch + 16 * s + 8 * hh));
+        sacc[0][0] = mfma32(a0, bq[0][s], s == 0 ? zero16 : sacc[0][0]);
+        sacc[1][0] = mfma32(a1, bq[0][s], s == 0 ? zero16 : sacc[1][0]);
+        sacc[0][1] = mfma32(a0, bq[1][s], s == 0 ? zero16 : sacc[0][1]);
+        sacc[1][1] = mfma32(a1, bq[1][s], s == 0 ? zero16 : sacc[1][1]);
       }
 
       const bool edge = (p.causal && key0 + kTile - 1 > pos_min_wg) || (key0 + kTile > L);
-      bf16x8 pb[2][2][2];  // [kb][half][cb]
+      uint32_t pk[2][2][2][4];  // [cb][kb][half][pair]
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        float sv[32];
+        const int lim = !edge ? 0x7fffffff : (p.causal ? min(pos[cb], L - 1) : L - 1);
+        auto mask = [&]() {
+          if (edge) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) sv[16 * kb + j] = sacc[kb][cb][j] * sl2;
-        if (edge) {
-          const int lim = p.causal ? min(pos[cb], L - 1) : L - 1;
+              for (int j = 0; j < 16; ++j) {
+                const int key = key0 + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
+                if (key > lim) sacc[kb][cb][j] = -INFINITY;
+              }
+          }
+        };
+        mask();
+        // Fast path: exponentiate against the current reference m.  It is
+        // valid while every p stays below 2^15 and the row has a reference;
+        // otherwise (rare: a new maximum, or the row's first live tile
+        // without a sink) the tile's scores are recomputed, the true row
+        // maximum taken, and O, d and m rescaled before exponentiating.
+        // exponentiate and pack: slot pair q of half hf <-> S^T entries
+        // j = 8 hf + 2 q, 8 hf + 2 q + 1 of key block kb
+        auto expo = [&](float neg_m) {
+          float acc = 0.f;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const int key = key0 + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
-              if (key > lim) sv[16 * kb + j] = -INFINITY;
-            }
-        }
-        float mx = sv[0];
+            for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int i = 1; i < 32; ++i) mx = fmaxf(mx, sv[i]);
-        mx = fmaxf(mx, xor_lane(mx, 32));
-        const float m_new = fmaxf(m[cb], mx);
-        const float alpha = (m[cb] == m_new) ? 1.f : fast_exp2(m[cb] - m_new);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        float ps = 0.f;
+              for (int q = 0; q < 4; ++q) {
+                const int j = 8 * hf + 2 * q;
+                const float e0 = fast_exp2(__builtin_fmaf(sacc[kb][cb][j], sl2, neg_m));
+                const float e1 = fast_exp2(__builtin_fmaf(sacc[kb][cb][j + 1], sl2, neg_m));
+                const uint32_t w = pack_bf16x2(e0, e1);
+                pk[cb][kb][hf][q] = w;
+                // sum the rounded values the MFMA consumes (v_dot2 with 1.0
+                // accumulates in fp32), so every row stays an exact convex
+                // combination of V
+                acc = dot2_sum(w, acc);
+              }
+          return acc;
+        };
+        float ds = expo((m[cb] == -INFINITY) ? 0.f : -m[cb]);
+        if (__any(!(ds <= kFastLimit) || m[cb] == -INFINITY)) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          sv[i] = fast_exp2(sv[i] - m_use);
-          ps += sv[i];
-        }
-        d[cb] = d[cb] * alpha + ps;
-        m[cb] = m_new;
-#pragma unroll
-        for (int db = 0; db < 2; ++db) o[cb][db] *= alpha;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const float* x = sv + 16 * kb + 8 * hf;
-            u32x4 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                       pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
-            pb[kb][hf][cb] = as_bf16x8(w);
+          for (int s = 0; s < 4; ++s) {
+            const bf16x8 a0 = as_bf16x8(
+                *reinterpret_cast<const u32x4*>(kbuf + r * kKPitch + 16 * s + 8 * hh));
+            const bf16x8 a1 = as_bf16x8(
+                *reinterpret_cast<const u32x4*>(kbuf + (32 + r) * kKPitch + 16 * s + 8 * hh));
+            sacc[0][cb] = mfma32(a0, bq[cb][s], s == 0 ? zero16 : sacc[0][cb]);
+            sacc[1][cb] = mfma32(a1, bq[cb][s], s == 0 ? zero16 : sacc[1][cb]);
           }
+          mask();
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; j += 2)
+              mx = fmaxf(fmaxf(mx, sacc[kb][cb][j]), sacc[kb][cb][j + 1]);
+          mx = fmaxf(mx, xor_lane(mx, 32));
+          const float m_new = fmaxf(m[cb], mx * sl2);
+          const float alpha = (m[cb] == m_new) ? 1.f : fast_exp2(m[cb] - m_new);
+          d[cb] *= alpha;
+          o[cb][0] *= alpha;
+          o[cb][1] *= alpha;
+          m[cb] = m_new;
+          ds = expo((m_new == -INFINITY) ? 0.f : -m_new);
+        }
+        d[cb] += ds;
       }
 
       // O^T[cb][db] += V^T[dims 32 db.., keys] P^T
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
+        for (int hf = 0; hf < 2; ++hf) {
+          const bf16x8 p0 = as_bf16x8(u32x4{pk[0][kb][hf][0], pk[0][kb][hf][1],
+                                            pk[0][kb][hf][2], pk[0][kb][hf][3]});
+          const bf16x8 p1 = as_bf16x8(u32x4{pk[1][kb][hf][0], pk[1][kb][hf][1],
+                                            pk[1][kb][hf][2], pk[1][kb][hf][3]});
+          const uint16_t* src = vbuf + (32 * kb + 16 * hf + tr_row) * kVPitch + tr_col;
 #pragma unroll
           for (int db = 0; db < 2; ++db) {
-            const uint16_t* vr = vbuf + (32 * db + r) * kVRow + 32 * kb + 16 * hf + 4 * hh;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
-            const u32x4 vw = {lo[0], lo[1], hi[0], hi[1]};
-            const bf16x8 a = as_bf16x8(vw);
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) o[cb][db] = mfma32(a, pb[kb][hf][cb], o[cb][db]);
+            const bf16x8 a = as_bf16x8(lds_tr16_pair(src + 32 * db, src + 8 * kVPitch + 32 * db));
+            o[0][db] = mfma32(a, p0, o[0][db]);
+            o[1][db] = mfma32(a, p1, o[1][db]);
           }
+        }
     }
     if (kt + 1 < n_tiles) store_tile(buf ^ 1);
     __syncthreads();

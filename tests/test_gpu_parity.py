@@ -1,6 +1,14 @@
 """GPU parity: the HIP path against the fp64 oracle on the same seeded bf16
-inputs.  Bar (per output tensor): max-abs <= 1e-2 and relative L2 <= 5e-3;
-the natural-log LSE within 2e-3 where finite and equal where infinite.
+inputs.  Bar (per output tensor): max-abs <= 1e-2 and relative L2 <= 5e-3,
+on fp32 outputs (the default); a bf16 output is additionally allowed its own
+final rounding, 2^-8 |ref| per element (bf16 unit roundoff), which alone can
+exceed 1e-2 once |o| > 2.56.  The natural-log LSE must be within 5e-3 where
+finite and equal where infinite.
+
+The LSE bound follows from the arithmetic: the kernels round every softmax
+weight to bf16 (relative error <= 2^-8) before both the P.V product and the
+denominator, so ln Z moves by at most ln(1 + 2^-8) = 3.9e-3; scores, exp2
+and log2 in fp32 add ~1e-6.  5e-3 leaves a margin over 3.9e-3.
 
 Each test names its case; everything calls the library through the C ABI
 (the thin Python binding) exactly as the benchmark does.
@@ -19,7 +27,8 @@ from tests._helpers import rel_l2  # noqa: E402
 
 MAX_ABS = 1e-2
 REL_L2 = 5e-3
-LSE_ABS = 2e-3
+LSE_ABS = 5e-3
+BF16_U = 2.0 ** -8
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -30,15 +39,21 @@ def _gpu():
     yield
 
 
+LAST_BF16 = [False]
+
+
 def gpu_run(b, out_dtype=None, stream=None):
     from gqa_attention_sinks_attn_amd import device
     db = device.to_device(b, out_dtype=out_dtype)
     device.run(db, stream=stream)
     torch.cuda.synchronize()
+    LAST_BF16[0] = db.out.dtype == torch.bfloat16
     return db.out.float().cpu().numpy().astype(np.float64), db.lse.cpu().numpy().astype(np.float64)
 
 
-def check(name, out, ref, lse=None, ref_lse=None):
+def check(name, out, ref, lse=None, ref_lse=None, bf16_out=None):
+    """bf16_out: None = the dtype of the last gpu_run."""
+    bf16_out = LAST_BF16[0] if bf16_out is None else bf16_out
     out = np.asarray(out, np.float64)
     ref = np.asarray(ref, np.float64)
     assert out.shape == ref.shape, name
@@ -46,8 +61,9 @@ def check(name, out, ref, lse=None, ref_lse=None):
     err = np.abs(out - ref)
     mx = float(err.max()) if err.size else 0.0
     rl = rel_l2(out, ref)
-    print(f"[{name}] max_abs={mx:.3e} rel_l2={rl:.3e}", flush=True)
-    assert mx <= MAX_ABS, f"{name}: max abs {mx}"
+    print(f"[{name}] max_abs={mx:.3e} rel_l2={rl:.3e} bf16_out={bf16_out}", flush=True)
+    allowed = MAX_ABS + (BF16_U * np.abs(ref) if bf16_out else 0.0)
+    assert np.all(err <= allowed), f"{name}: max abs {mx} (worst excess {float((err - allowed).max())})"
     if np.linalg.norm(ref) > 1e-6:
         assert rl <= REL_L2, f"{name}: rel L2 {rl}"
     if lse is not None:
@@ -236,7 +252,7 @@ def test_merge_against_oracle_partials():
     lse = torch.empty((6, 8), dtype=torch.float32, device="cuda")
     sink_attn_merge(o_t, l_t, 6, 8, S, 64, out, F32, lse)
     torch.cuda.synchronize()
-    check("merge", out.cpu().numpy(), ref, lse.cpu().numpy().astype(np.float64), rl)
+    check("merge", out.cpu().numpy(), ref, lse.cpu().numpy().astype(np.float64), rl, bf16_out=False)
     assert np.all(out.cpu().numpy()[5, 0] == 0) and lse.cpu().numpy()[5, 0] == -np.inf
 
 
@@ -253,4 +269,65 @@ def test_deterministic_and_stream_aware():
     s.synchronize()
     assert torch.equal(first, db.out)
     ref, rl = oracle.attend(b)
-    check("decode side stream", db.out.float().cpu().numpy(), ref, db.lse.cpu().numpy(), rl)
+    check("decode side stream", db.out.float().cpu().numpy(), ref, db.lse.cpu().numpy(), rl,
+          bf16_out=db.out.dtype == torch.bfloat16)
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+@pytest.mark.parametrize("case", ["very_negative_no_sink", "very_positive_zero_sink", "growing_keys"])
+def test_extreme_score_ranges(kind, case):
+    """Score ranges that force every rescale path: scores near -128 with no
+    sink (a reference of 0 would underflow), near +128 with a zero sink
+    (overflow against the sink's reference), and keys whose scores grow
+    along the sequence (the running maximum moves many times)."""
+    qlens = [1, 1, 1] if kind == "decode" else [150, 1, 64]
+    b = W.make_batch(81, kind=kind, qlens=qlens, kv_lens=[300, 77, 64], hq=16, hkv=2,
+                     paged=True, sinks=None if case == "very_negative_no_sink" else 0.0,
+                     num_splits=3)
+    qf = W.bf16_bits_to_f32(b.q)
+    kf = W.bf16_bits_to_f32(b.k)
+    if case == "very_negative_no_sink":
+        qf = np.full_like(qf, 4.0)
+        kf = np.full_like(kf, -4.0) + np.round(kf * 4) / 64   # q.k/8 ~ -128 +- small
+    elif case == "very_positive_zero_sink":
+        qf = np.full_like(qf, 4.0)
+        kf = np.full_like(kf, 4.0) + np.round(kf * 4) / 64
+    else:
+        # scale each cache slot by its position inside its page so that later
+        # keys in every page score higher (and the maximum keeps moving)
+        kf = kf * (1.0 + np.arange(16, dtype=np.float32)[None, None, :, None] / 4.0)
+    b.q = W.to_bf16_bits(qf)
+    b.k = W.to_bf16_bits(kf)
+    out, lse = gpu_run(b)
+    ref, rl = oracle.attend(b)
+    check(f"{kind} {case}", out, ref, lse, rl)
+
+
+def test_decode_many_and_empty_requests():
+    """Thousands of short requests, empty requests (kv_len 0, non-causal so
+    the definition allows them) and one-page requests, called twice on the
+    same workspace."""
+    rng = np.random.default_rng(5)
+    L = rng.integers(0, 40, size=4500)
+    L[:7] = 0
+    L[-3:] = 0
+    L[100:110] = 16
+    b = W.make_batch(91, kind="decode", qlens=[1] * L.size, kv_lens=L, hq=8, hkv=2, paged=True,
+                     sinks="normal", causal=False, num_splits=0)
+    from gqa_attention_sinks_attn_amd import device
+    db = device.to_device(b)
+    ref, rl = oracle.attend(b)
+    for call in range(2):
+        device.run(db)
+        torch.cuda.synchronize()
+        check(f"decode many requests, call {call}", db.out.float().cpu().numpy(), ref,
+              db.lse.cpu().numpy().astype(np.float64), rl, bf16_out=False)
+
+
+@pytest.mark.parametrize("lens", [[1], [16] * 64, [17, 4096, 1, 2000], [131072, 3]])
+def test_decode_length_mixes(lens):
+    b = W.make_batch(93 + len(lens), kind="decode", qlens=[1] * len(lens), kv_lens=lens, hq=64,
+                     hkv=8, paged=True, sinks="normal", num_splits=0)
+    out, lse = gpu_run(b)
+    ref, rl = oracle.attend(b)
+    check(f"decode length mix {lens[:4]}", out, ref, lse, rl)

@@ -79,7 +79,7 @@ class Batch:
     page_size: int
     sm_scale: float
     causal: bool
-    out_dtype: str = "bf16"         # "bf16" or "f32"
+    out_dtype: str = "f32"          # "f32" or "bf16"
     num_splits: int = 0             # decode: 0 = library's automatic plan
     name: str = ""
 
@@ -180,7 +180,7 @@ def _draw_sinks(rng, hq: int, sinks, std: float = 1.0) -> Optional[np.ndarray]:
 def make_batch(seed, *, kind: str, qlens: Sequence[int], kv_lens: Sequence[int],
                hq: int, hkv: int, d: int = HEAD_DIM, paged: bool = False,
                page_size: int = PAGE_SIZE, sinks="normal", sink_std: float = 1.0,
-               causal: bool = True, out_dtype: str = "bf16", num_splits: int = 0,
+               causal: bool = True, out_dtype: str = "f32", num_splits: int = 0,
                sm_scale: Optional[float] = None, permute_pages: bool = True,
                name: str = "") -> Batch:
     """Draw one batch.  `seed` is an int or a numpy Generator that has already
