@@ -12,10 +12,13 @@
 // time, round robin, each keeping its own online state for the G query heads
 // of KV head g; the four states are merged in LDS at the end.  Per two-page
 // step a wave:
-//   * takes the two page ids from a register that holds the ids of its next
-//     32 steps (one vector load per 32 steps, read back with readlane),
-//   * has already issued the step's K and V loads one step earlier (software
-//     pipeline, two register sets in flight per wave),
+//   * takes the two page ids from a register that holds its next 32 steps'
+//     ids (one vector load per 32 steps, outside the step loop, read back
+//     with readlane) and has issued the step's K and V loads one step
+//     earlier (software pipeline, two register sets in flight per wave; the
+//     issue is unconditional -- past the end it repeats the last step's
+//     pages, which the cache serves -- so the compiler only waits for the
+//     step being processed),
 //   * computes S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (16 keys x 16 head
 //     columns; columns >= G are padding) with K straight from registers,
 //   * updates m, d and O in the exp2 domain, and
@@ -46,6 +49,12 @@ constexpr int kLdsBytes =
         ? (kWaves * kWaveLds * 2)
         : (kWaves * (int)sizeof(CombineSlot));
 
+// Complete the loads feeding `x` here (an empty asm reading the register).
+template <class T>
+__device__ __forceinline__ void settle(const T& x) {
+  asm volatile("" ::"v"(x));
+}
+
 struct StepRegs {
   u32x4 k00, k01, k10, k11;   // K: page 0/1, dims 8 grp + {0, 32}
   u32x4 v00, v01, v10, v11;   // V: page 0/1, 32 contiguous bytes each
@@ -61,17 +70,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
   const int g = unit % p.hkv;
   const int b = unit / p.hkv;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index in an SGPR: everything derived from it (page ranges, page-id
+  // addresses) stays scalar, so page ids come through scalar loads
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;     // head column of the MFMA tile
   const int grp = lane >> 4;     // lane group 0..3
   const bool live_col = col < G;
   const int h = g * G + (live_col ? col : 0);
 
-  const int L = p.kv_len[b];
+  const int L = __builtin_amdgcn_readfirstlane(p.kv_len[b]);
   const int n_pages = (L + kPage - 1) / kPage;
   const int pg0 = c * p.chunk_pages;
   const int pg1 = min(n_pages, pg0 + p.chunk_pages);
-  const int32_t* pages = p.page_indices + p.page_indptr[b];
+  const int32_t* pages = p.page_indices + __builtin_amdgcn_readfirstlane(p.page_indptr[b]);
 
   // Q^T operand: column `col` = head h, k-step s covers dims 32 s + 8 grp .. +7.
   bf16x8 bq0, bq1;
@@ -99,24 +110,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
   const int koff = col * kD + 8 * grp;                       // K operand offset
   const int voff = (lane >> 2) * kD + 16 * (lane & 3);       // V: 32 B per lane
 
-  // Page ids of this wave's next 32 steps: lane l holds step l / 2, page l % 2.
+  // Page ids: one vector load per block of 32 steps (lane l holds the id of
+  // page l % 2 of step l / 2), placed outside the step loop and completed
+  // there, then read with readlane.  Step `st` covers pages first + 8 st and
+  // first + 8 st + 1 of the request.
   const int first = pg0 + 2 * wave;
+  const int n_steps = pg1 > first ? (pg1 - first + 7) / 8 : 0;
+  struct Pids { int a, b; };
   int ids = 0;
-  auto load_ids = [&](int step0) {
-    const int idx = first + 8 * (step0 + (lane >> 1)) + (lane & 1);
-    ids = idx < pg1 ? pages[idx] : 0;
+  auto pids = [&](int st) -> Pids {   // st: step index inside the current block
+    return Pids{__builtin_amdgcn_readlane(ids, 2 * st), __builtin_amdgcn_readlane(ids, 2 * st + 1)};
   };
 
-  auto issue = [&](StepRegs& r, int step) {
-    const int slot = 2 * (step & 31);
-    const int pp = first + 8 * step;
-    const bool two = (pp + 1) < pg1;
-    const int pid0 = __builtin_amdgcn_readlane(ids, slot);
-    const int pid1 = two ? __builtin_amdgcn_readlane(ids, slot + 1) : pid0;
-    const uint16_t* kb0 = p.k + pid0 * page_stride + g * head_stride;
-    const uint16_t* vb0 = p.v + pid0 * page_stride + g * head_stride;
-    const uint16_t* kb1 = p.k + pid1 * page_stride + g * head_stride;
-    const uint16_t* vb1 = p.v + pid1 * page_stride + g * head_stride;
+  auto issue = [&](StepRegs& r, Pids ids) {
+    const uint16_t* kb0 = p.k + ids.a * page_stride + g * head_stride;
+    const uint16_t* vb0 = p.v + ids.a * page_stride + g * head_stride;
+    const uint16_t* kb1 = p.k + ids.b * page_stride + g * head_stride;
+    const uint16_t* vb1 = p.v + ids.b * page_stride + g * head_stride;
     r.k00 = ld16(kb0 + koff);
     r.k01 = ld16(kb0 + koff + 32);
     r.k10 = ld16(kb1 + koff);
@@ -193,25 +203,29 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
     o3 = mfma16(as_bf16x8(lds_tr16_pair(src + 48, src + kPage * kVPitch + 48)), pb, o3);
   };
 
-  const int n_steps = pg1 > first ? (pg1 - first + 7) / 8 : 0;
-  if (n_steps > 0) {
-    load_ids(0);
+  // Software pipeline: loads for step st + 1 are issued before step st is
+  // processed, unconditionally (past the block's last step they repeat it;
+  // the cache serves the repeat), so the compiler waits only for the step
+  // being processed.  sched_barrier pins the issue/process order.
+  for (int blk = 0; blk < n_steps; blk += 32) {
+    const int nb = min(32, n_steps - blk);
+    {
+      const int st = blk + min(lane >> 1, nb - 1);
+      const int pp = first + 8 * st;
+      ids = pages[min(pp + (lane & 1), pg1 - 1)];
+      settle(ids);
+    }
     StepRegs ra, rb;
-    issue(ra, 0);
-    int step = 0;
-    while (true) {
-      if (step + 1 < n_steps) {
-        if (((step + 1) & 31) == 0) load_ids(step + 1);
-        issue(rb, step + 1);
-      }
-      process(ra, step);
-      if (++step >= n_steps) break;
-      if (step + 1 < n_steps) {
-        if (((step + 1) & 31) == 0) load_ids(step + 1);
-        issue(ra, step + 1);
-      }
-      process(rb, step);
-      if (++step >= n_steps) break;
+    issue(ra, pids(0));
+    for (int i = 0; i < nb; i += 2) {
+      issue(rb, pids(min(i + 1, nb - 1)));
+      __builtin_amdgcn_sched_barrier(0);
+      process(ra, blk + i);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ra, pids(min(i + 2, nb - 1)));
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < nb) process(rb, blk + i + 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 

@@ -81,8 +81,6 @@ def to_device(b, device="cuda", with_lse: bool = True, out_dtype=None) -> Device
     if db.kind == "decode":
         db.workspace_bytes = sink_attn_decode_workspace_size(
             db.batch, db.num_qo_heads, db.num_kv_heads, db.head_dim, db.max_kv_len, db.num_splits)
-        # zero-filled once: the balanced decode keeps completion counters in
-        # the workspace and leaves them at zero after every call
         db.workspace = (torch.zeros(db.workspace_bytes, dtype=torch.uint8, device=device)
                         if db.workspace_bytes else None)
     return db
