@@ -4,17 +4,20 @@
 Default workload: paged decode, batch 64, KV lengths uniform in [1, 4096],
 64 query / 8 KV heads, head_dim 64, 16-token pages with a permuted page table
 (the decode workload the headline metric is quoted on).  One step = one
-pass of the decode path with the library's automatic split plan: the
-split-KV partial kernel (sink_attn_decode_partial) followed by the LSE merge
-(sink_attn_merge), both through the C ABI.  Metric: KV bytes read per second
-(2 * Hkv * 64 * 2 B per KV token) over the whole step.
+pass of the decode path the library's automatic plan takes for it: the
+load-balanced first pass (sink_attn_decode_balanced_partial, every wave
+streaming an equal share of the batch's pages) followed by its finish pass
+(sink_attn_decode_balanced_finish, the LSE merge of requests that span
+several ranges), both through the C ABI.  Metric: KV bytes read per second
+(2 * Hkv * 64 * 2 B per KV token) over the whole step.  --decode-plan
+chunked times the split-KV pair (sink_attn_decode_partial +
+sink_attn_merge) instead.
 
 Also reported, on the same JSON line:
-  * "roofline": the dominant kernel (decode partial) -- algorithmic bytes
+  * "roofline": the dominant kernel (the first pass) -- algorithmic bytes
     per launch / its mean launch time from HIP events around it on its own
-    stream,
-    against the 8 TB/s HBM peak; "traffic" from rocprofv3 counters when a
-    measurement for the current kernel exists, else null;
+    stream, against the 8 TB/s HBM peak; "traffic" from rocprofv3 counters
+    when a measurement for the current kernel exists, else null;
   * "prefill": the causal prefill workload (8 x 4096 tokens, 64/8 heads,
     contiguous KV) in TFLOP/s against the 2.5 PFLOP/s dense bf16 peak;
   * "cpu_baseline": the fp64 oracle timed on this host's cores on the same
@@ -25,7 +28,7 @@ Also reported, on the same JSON line:
 
 --mode traffic runs, untimed: a plain 256 MiB device-to-device copy three
 times (the calibration dispatch for FETCH_SIZE / WRITE_SIZE), then the decode
-partial kernel eight times on the decode workload (rotating the same four KV
+first pass eight times on the decode workload (rotating the same four KV
 copies as the timed run), then the prefill kernel three times.
 """
 from __future__ import annotations
@@ -48,8 +51,8 @@ KV_COPIES = 4                  # rotated KV pools: 4 x 269 MB > 256 MB last-leve
 # HBM bytes per dispatch from rocprofv3 FETCH_SIZE + WRITE_SIZE passes
 # (python bench.py --mode traffic), each scaled by the same counter on a
 # 256 MiB copy; see profiles/.  Valid for the kernel sources they were taken
-# on -- reset to None whenever decode.hip or prefill.hip changes.
-DECODE_TRAFFIC_BYTES = None
+# on -- reset to None whenever decode_balanced.hip or prefill.hip changes.
+DECODE_TRAFFIC_BYTES = 260_966_351
 PREFILL_TRAFFIC_BYTES = 1_362_741_767
 
 
@@ -78,26 +81,50 @@ def prefill_pairs(b) -> int:
 
 def bench_decode(args, torch, sa, device, W):
     b = W.config(2)
-    db = device.to_device(b)
-    S = device.splits_of(db)
+    balanced = args.decode_plan == "balanced"
+    db = device.to_device(b, plan="balanced" if balanced else "chunked")
     B, Hq, D = db.batch, db.num_qo_heads, db.head_dim
-    o_parts = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
-    lse_parts = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
     out_code = sa.F32 if db.out.dtype == torch.float32 else sa.BF16
+    if balanced:
+        R = sa.sink_attn_decode_num_ranges(B, db.num_kv_heads, db.max_kv_len, 0)
+        plan = dict(num_ranges=R)
+    else:
+        S = device.splits_of(db)
+        o_parts = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
+        lse_parts = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+        plan = dict(num_splits=S)
     ks = [db.k] + [db.k.clone() for _ in range(KV_COPIES - 1)]
     vs = [db.v] + [db.v.clone() for _ in range(KV_COPIES - 1)]
     torch.cuda.synchronize()
+
+    def first(k, v):
+        if balanced:
+            sa.sink_attn_decode_balanced_partial(
+                db.q, k, v, db.kv_indptr, db.page_indices, db.kv_len, db.sinks, B, Hq,
+                db.num_kv_heads, D, db.page_size, db.max_kv_len, 0, db.sm_scale, db.out,
+                out_code, db.lse, db.workspace, db.workspace_bytes)
+        else:
+            sa.sink_attn_decode_partial(db.q, k, v, db.kv_indptr, db.page_indices, db.kv_len,
+                                        db.sinks, B, Hq, db.num_kv_heads, D, db.page_size,
+                                        db.max_kv_len, db.num_splits, db.sm_scale, o_parts,
+                                        lse_parts)
+
+    def second():
+        if balanced:
+            sa.sink_attn_decode_balanced_finish(db.kv_indptr, db.sinks, B, Hq, db.num_kv_heads, D,
+                                                db.max_kv_len, 0, db.out, out_code, db.lse,
+                                                db.workspace, db.workspace_bytes)
+        else:
+            sa.sink_attn_merge(o_parts, lse_parts, B, Hq, S, D, db.out, out_code, db.lse)
 
     def step(i, ev=None):
         k, v = ks[i % KV_COPIES], vs[i % KV_COPIES]
         if ev is not None:
             ev[0].record()
-        sa.sink_attn_decode_partial(db.q, k, v, db.kv_indptr, db.page_indices, db.kv_len, db.sinks,
-                                    B, Hq, db.num_kv_heads, D, db.page_size, db.max_kv_len,
-                                    db.num_splits, db.sm_scale, o_parts, lse_parts)
+        first(k, v)
         if ev is not None:
             ev[1].record()
-        sa.sink_attn_merge(o_parts, lse_parts, B, Hq, S, D, db.out, out_code, db.lse)
+        second()
 
     for i in range(args.warmup):
         step(i)
@@ -117,8 +144,8 @@ def bench_decode(args, torch, sa, device, W):
     kv_bytes = int(b.kv_len.astype(np.int64).sum()) * 2 * b.num_kv_heads * b.head_dim * 2
     alg = decode_algorithmic_bytes(b)
     ms_step = total_ms / args.steps
-    res = dict(batch=b, db=db, S=S, ms_step=ms_step, kern_ms=kern_ms, kv_bytes=kv_bytes,
-               alg_bytes=alg, value=kv_bytes / (ms_step * 1e-3) / 1e9)
+    res = dict(batch=b, db=db, plan=plan, ms_step=ms_step, kern_ms=kern_ms, kv_bytes=kv_bytes,
+               alg_bytes=alg, value=kv_bytes / (ms_step * 1e-3) / 1e9, first=first)
     return res
 
 
@@ -173,20 +200,18 @@ def traffic_run(torch, sa, device, W):
     torch.cuda.synchronize()
     log(f"[traffic] copy: {x.numel() * 4} bytes read and written per dispatch")
     b = W.config(2)
-    db = device.to_device(b)
-    S = device.splits_of(db)
+    db = device.to_device(b, plan="balanced")
     B, Hq, D = db.batch, db.num_qo_heads, db.head_dim
-    op = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
-    lp = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    out_code = sa.F32 if db.out.dtype == torch.float32 else sa.BF16
     ks = [db.k] + [db.k.clone() for _ in range(KV_COPIES - 1)]
     vs = [db.v] + [db.v.clone() for _ in range(KV_COPIES - 1)]
     for i in range(8):
-        sa.sink_attn_decode_partial(db.q, ks[i % KV_COPIES], vs[i % KV_COPIES], db.kv_indptr,
-                                    db.page_indices, db.kv_len, db.sinks, B, Hq, db.num_kv_heads,
-                                    D, db.page_size, db.max_kv_len, db.num_splits, db.sm_scale,
-                                    op, lp)
+        sa.sink_attn_decode_balanced_partial(
+            db.q, ks[i % KV_COPIES], vs[i % KV_COPIES], db.kv_indptr, db.page_indices, db.kv_len,
+            db.sinks, B, Hq, db.num_kv_heads, D, db.page_size, db.max_kv_len, 0, db.sm_scale,
+            db.out, out_code, db.lse, db.workspace, db.workspace_bytes)
     torch.cuda.synchronize()
-    log(f"[traffic] decode partial: {decode_algorithmic_bytes(b)} algorithmic bytes per dispatch")
+    log(f"[traffic] decode first pass: {decode_algorithmic_bytes(b)} algorithmic bytes per dispatch")
     pb = W.config(4)
     pdb = device.to_device(pb, with_lse=False)
     for _ in range(3):
@@ -204,6 +229,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--mode", choices=["bench", "traffic"], default="bench")
+    ap.add_argument("--decode-plan", choices=["balanced", "chunked"], default="balanced",
+                    help="decode kernels to time (default: the automatic plan's, balanced)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus "
@@ -255,14 +282,17 @@ def main():
             "workload": W.CONFIG_NAMES[2],
             "batch": b.batch, "kv_tokens": int(b.kv_len.sum()), "num_qo_heads": b.num_qo_heads,
             "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "page_size": b.page_size,
-            "num_splits": dec["S"], "kv_copies_rotated": KV_COPIES, "out_dtype": "f32",
-            "step": "sink_attn_decode_partial + sink_attn_merge",
+            **dec["plan"], "kv_copies_rotated": KV_COPIES, "out_dtype": "f32",
+            "step": ("sink_attn_decode_balanced_partial + sink_attn_decode_balanced_finish"
+                     if args.decode_plan == "balanced"
+                     else "sink_attn_decode_partial + sink_attn_merge"),
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": DECODE_TRAFFIC_BYTES,
-            "kernel": "decode_kernel<8> (split-KV partial)",
+            "traffic": DECODE_TRAFFIC_BYTES if args.decode_plan == "balanced" else None,
+            "kernel": ("decode_balanced_kernel<8> (first pass)" if args.decode_plan == "balanced"
+                       else "decode_kernel<8> (split-KV partial)"),
             "kernel_ms": round(dec["kern_ms"], 5), "algorithmic_bytes": dec["alg_bytes"],
         },
         "cpu_baseline": cpu,

@@ -21,6 +21,9 @@ __all__ = [
     "SinkAttnError", "LIB_PATH", "lib", "BF16", "F32",
     "sink_attn_prefill", "sink_attn_decode", "sink_attn_decode_partial", "sink_attn_merge",
     "sink_attn_decode_workspace_size", "sink_attn_decode_num_splits",
+    "sink_attn_decode_balanced", "sink_attn_decode_balanced_partial",
+    "sink_attn_decode_balanced_finish", "sink_attn_decode_balanced_workspace_size",
+    "sink_attn_decode_num_ranges",
     "sink_attn_status_string", "sink_attn_last_error", "sink_attn_version",
     "SYMBOLS",
 ]
@@ -31,6 +34,9 @@ F32 = 1
 SYMBOLS = (
     "sink_attn_prefill", "sink_attn_decode", "sink_attn_decode_partial", "sink_attn_merge",
     "sink_attn_decode_workspace_size", "sink_attn_decode_num_splits",
+    "sink_attn_decode_balanced", "sink_attn_decode_balanced_partial",
+    "sink_attn_decode_balanced_finish", "sink_attn_decode_balanced_workspace_size",
+    "sink_attn_decode_num_ranges",
     "sink_attn_status_string", "sink_attn_last_error", "sink_attn_version",
 )
 
@@ -73,6 +79,18 @@ def lib():
     L.sink_attn_decode_workspace_size.restype = ctypes.c_size_t
     L.sink_attn_decode_num_splits.argtypes = [_I, _I, _I, _I, _I]
     L.sink_attn_decode_num_splits.restype = _I
+    for name in ("sink_attn_decode_balanced", "sink_attn_decode_balanced_partial"):
+        f = getattr(L, name)
+        f.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
+                      ctypes.c_int, _P, _P, ctypes.c_size_t, _P]
+        f.restype = ctypes.c_int
+    L.sink_attn_decode_balanced_finish.argtypes = [_P, _P, _I, _I, _I, _I, _I, _I, _P,
+                                                   ctypes.c_int, _P, _P, ctypes.c_size_t, _P]
+    L.sink_attn_decode_balanced_finish.restype = ctypes.c_int
+    L.sink_attn_decode_balanced_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
+    L.sink_attn_decode_balanced_workspace_size.restype = ctypes.c_size_t
+    L.sink_attn_decode_num_ranges.argtypes = [_I, _I, _I, _I]
+    L.sink_attn_decode_num_ranges.restype = _I
     L.sink_attn_status_string.argtypes = [ctypes.c_int]
     L.sink_attn_status_string.restype = ctypes.c_char_p
     L.sink_attn_last_error.argtypes = []
@@ -179,3 +197,55 @@ def sink_attn_merge(o_parts, lse_parts, num_rows, num_heads, num_splits, head_di
     _check(lib().sink_attn_merge(
         _ptr(o_parts), _ptr(lse_parts), int(num_rows), int(num_heads), int(num_splits),
         int(head_dim), _ptr(out), _dtype_code(out_dtype), _ptr(lse_out), _stream(stream)))
+
+
+def sink_attn_decode_num_ranges(batch, num_kv_heads, max_kv_len, num_ranges) -> int:
+    return int(lib().sink_attn_decode_num_ranges(int(batch), int(num_kv_heads), int(max_kv_len),
+                                                int(num_ranges)))
+
+
+def sink_attn_decode_balanced_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim,
+                                             max_kv_len, num_ranges) -> int:
+    return int(lib().sink_attn_decode_balanced_workspace_size(
+        int(batch), int(num_qo_heads), int(num_kv_heads), int(head_dim), int(max_kv_len),
+        int(num_ranges)))
+
+
+def _balanced(fn, q, k_pages, v_pages, page_indptr, page_indices, kv_len, sinks, batch,
+              num_qo_heads, num_kv_heads, head_dim, page_size, max_kv_len, num_ranges, sm_scale,
+              out, out_dtype, lse, workspace, workspace_bytes, stream):
+    _check(fn(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_indptr), _ptr(page_indices),
+        _ptr(kv_len), _ptr(sinks), int(batch), int(num_qo_heads), int(num_kv_heads),
+        int(head_dim), int(page_size), int(max_kv_len), int(num_ranges), float(sm_scale),
+        _ptr(out), _dtype_code(out_dtype), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+        _stream(stream)))
+
+
+def sink_attn_decode_balanced(q, k_pages, v_pages, page_indptr, page_indices, kv_len, sinks,
+                              batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                              max_kv_len, num_ranges, sm_scale, out, out_dtype, lse,
+                              workspace, workspace_bytes, stream=None) -> None:
+    _balanced(lib().sink_attn_decode_balanced, q, k_pages, v_pages, page_indptr, page_indices,
+              kv_len, sinks, batch, num_qo_heads, num_kv_heads, head_dim, page_size, max_kv_len,
+              num_ranges, sm_scale, out, out_dtype, lse, workspace, workspace_bytes, stream)
+
+
+def sink_attn_decode_balanced_partial(q, k_pages, v_pages, page_indptr, page_indices, kv_len,
+                                      sinks, batch, num_qo_heads, num_kv_heads, head_dim,
+                                      page_size, max_kv_len, num_ranges, sm_scale, out,
+                                      out_dtype, lse, workspace, workspace_bytes,
+                                      stream=None) -> None:
+    _balanced(lib().sink_attn_decode_balanced_partial, q, k_pages, v_pages, page_indptr,
+              page_indices, kv_len, sinks, batch, num_qo_heads, num_kv_heads, head_dim,
+              page_size, max_kv_len, num_ranges, sm_scale, out, out_dtype, lse, workspace,
+              workspace_bytes, stream)
+
+
+def sink_attn_decode_balanced_finish(page_indptr, sinks, batch, num_qo_heads, num_kv_heads,
+                                     head_dim, max_kv_len, num_ranges, out, out_dtype, lse,
+                                     workspace, workspace_bytes, stream=None) -> None:
+    _check(lib().sink_attn_decode_balanced_finish(
+        _ptr(page_indptr), _ptr(sinks), int(batch), int(num_qo_heads), int(num_kv_heads),
+        int(head_dim), int(max_kv_len), int(num_ranges), _ptr(out), _dtype_code(out_dtype),
+        _ptr(lse), _ptr(workspace), int(workspace_bytes), _stream(stream)))

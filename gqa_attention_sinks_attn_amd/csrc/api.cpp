@@ -71,6 +71,59 @@ int32_t plan_splits(int32_t batch, int32_t hkv, int32_t max_kv_len, int32_t requ
   return (int32_t)s;
 }
 
+// Load-balanced plan: the batch's pages are cut, per KV head, into n_ranges
+// equal ranges (a multiple of 4: one workgroup holds four ranges, one per
+// wave).  Every range carries the same work, so the grid must spread evenly
+// over the compute units: the automatic plan launches at most one workgroup
+// per CU (kTargetWorkgroups), i.e. one streaming wave per SIMD, which keeps
+// two K/V steps in flight per wave -- enough to saturate HBM -- and makes
+// the ranges as long as possible, so the start-up of a wave and the merge of
+// a request's partials stay small against its streaming.  Ranges shorter
+// than kMinRangePages pages are not worth a wave.  An explicit request takes
+// exactly that many ranges (rounded up to a multiple of 4) and allows ranges
+// down to one page.
+#ifndef SA_TARGET_WORKGROUPS
+#define SA_TARGET_WORKGROUPS 256
+#endif
+#ifndef SA_MIN_RANGE_PAGES
+#define SA_MIN_RANGE_PAGES 8
+#endif
+constexpr int64_t kTargetWorkgroups = SA_TARGET_WORKGROUPS;
+constexpr int32_t kMinRangePages = SA_MIN_RANGE_PAGES;
+constexpr int32_t kMaxRanges = 1 << 20;
+
+struct RangePlan {
+  int32_t n_ranges;
+  int32_t min_pages;
+};
+
+RangePlan plan_ranges(int32_t batch, int32_t hkv, int32_t max_kv_len, int32_t requested) {
+  int64_t r;
+  int32_t min_pages;
+  if (requested > 0) {
+    r = (requested + 3) / 4 * 4;
+    min_pages = 1;
+  } else {
+    const int64_t pages_ub = (int64_t)batch * ((max_kv_len + kPageSize - 1) / kPageSize);
+    const int64_t wgs_per_head = kTargetWorkgroups / hkv;
+    r = 4 * (wgs_per_head > 1 ? wgs_per_head : 1);
+    const int64_t by_len = (pages_ub + kMinRangePages - 1) / kMinRangePages;
+    if (r > by_len) r = (by_len + 3) / 4 * 4;
+    min_pages = kMinRangePages;
+  }
+  if (r > kMaxRanges) r = kMaxRanges;
+  if (r < 4) r = 4;
+  return RangePlan{(int32_t)r, min_pages};
+}
+
+size_t balanced_slots(int32_t batch, int32_t n_ranges) { return (size_t)n_ranges + batch - 1; }
+
+// sink_attn_decode's automatic plan: requests longer than 16 pages go to the
+// load-balanced plan; shorter ones fit one chunk, written by one kernel.
+bool auto_uses_balanced(int32_t max_kv_len, int32_t num_splits) {
+  return num_splits == 0 && (max_kv_len + kPageSize - 1) / kPageSize > 16;
+}
+
 int32_t chunk_pages_for(int32_t max_kv_len, int32_t splits) {
   const int32_t pages = (max_kv_len + kPageSize - 1) / kPageSize;
   int32_t cp = (pages + splits - 1) / splits;
@@ -110,9 +163,31 @@ size_t sink_attn_decode_workspace_size(int32_t batch, int32_t num_qo_heads, int3
   if (batch <= 0 || num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_kv_len < 0 ||
       num_splits < 0)
     return 0;
+  if (auto_uses_balanced(max_kv_len, num_splits))
+    return sink_attn_decode_balanced_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim,
+                                                    max_kv_len, 0);
   const int32_t s = plan_splits(batch, num_kv_heads, max_kv_len, num_splits);
   if (s <= 1) return 0;
   const size_t rows = (size_t)batch * num_qo_heads * s;
+  const size_t o_bytes = rows * head_dim * sizeof(float);
+  const size_t l_bytes = rows * sizeof(float);
+  return o_bytes + ((l_bytes + 255) / 256) * 256;
+}
+
+int32_t sink_attn_decode_num_ranges(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len,
+                                    int32_t num_ranges) {
+  if (batch <= 0 || num_kv_heads <= 0 || max_kv_len < 0 || num_ranges < 0) return 4;
+  return plan_ranges(batch, num_kv_heads, max_kv_len, num_ranges).n_ranges;
+}
+
+size_t sink_attn_decode_balanced_workspace_size(int32_t batch, int32_t num_qo_heads,
+                                                int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t max_kv_len, int32_t num_ranges) {
+  if (batch <= 0 || num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_kv_len < 0 ||
+      num_ranges < 0)
+    return 0;
+  const RangePlan plan = plan_ranges(batch, num_kv_heads, max_kv_len, num_ranges);
+  const size_t rows = balanced_slots(batch, plan.n_ranges) * num_qo_heads;
   const size_t o_bytes = rows * head_dim * sizeof(float);
   const size_t l_bytes = rows * sizeof(float);
   return o_bytes + ((l_bytes + 255) / 256) * 256;
@@ -311,6 +386,11 @@ sink_attn_status sink_attn_decode(const void* q, const void* k_pages, const void
   if (!aligned(out, 16) || (lse && !aligned(lse, 4)))
     return fail(SINK_ATTN_ERR_MISALIGNED, "decode: out must be 16-byte and lse 4-byte aligned");
 
+  if (auto_uses_balanced(max_kv_len, num_splits))
+    return sink_attn_decode_balanced(q, k_pages, v_pages, page_indptr, page_indices, kv_len, sinks,
+                                     batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                     max_kv_len, 0, sm_scale, out, out_dtype, lse, workspace,
+                                     workspace_bytes, stream);
   const int32_t S = plan_splits(batch, num_kv_heads, max_kv_len, num_splits);
   const size_t need = sink_attn_decode_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim,
                                                       max_kv_len, num_splits);
@@ -349,6 +429,131 @@ sink_attn_status sink_attn_decode(const void* q, const void* k_pages, const void
   m.out_f32 = a.out_f32;
   m.lse = lse;
   return hip_status(sa::launch_merge(m, s), "decode merge launch");
+}
+
+namespace {
+
+// Validation and argument set-up shared by the three balanced entry points.
+// `stage`: 1 = partial pass, 2 = finish, 3 = both.
+sink_attn_status balanced_setup(const void* q, const void* k_pages, const void* v_pages,
+                                const int32_t* page_indptr, const int32_t* page_indices,
+                                const int32_t* kv_len, const float* sinks, int32_t batch,
+                                int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t page_size, int32_t max_kv_len, int32_t num_ranges,
+                                float sm_scale, void* out, sink_attn_dtype out_dtype, float* lse,
+                                void* workspace, size_t workspace_bytes, int stage,
+                                sa::BalancedDecodeArgs* a) {
+  const char* who = stage == 1 ? "decode_balanced_partial"
+                    : stage == 2 ? "decode_balanced_finish" : "decode_balanced";
+  if (stage & 1) {
+    sink_attn_status st = check_decode_common(q, k_pages, v_pages, page_indptr, page_indices,
+                                              kv_len, sinks, batch, num_qo_heads, num_kv_heads,
+                                              head_dim, page_size, max_kv_len, 0, sm_scale);
+    if (st != SINK_ATTN_OK) return st;
+  } else {
+    if (!page_indptr) return fail(SINK_ATTN_ERR_NULL_ARG, "%s: page_indptr is required", who);
+    if (batch <= 0 || max_kv_len < 0)
+      return fail(SINK_ATTN_ERR_BAD_SHAPE, "%s: batch=%d max_kv_len=%d", who, batch, max_kv_len);
+    sink_attn_status st = check_heads(num_qo_heads, num_kv_heads, true);
+    if (st != SINK_ATTN_OK) return st;
+    if (head_dim != kHeadDim)
+      return fail(SINK_ATTN_ERR_UNSUPPORTED, "%s: head_dim=%d (only 64 is built)", who, head_dim);
+    if (!aligned(page_indptr, 4) || (sinks && !aligned(sinks, 4)))
+      return fail(SINK_ATTN_ERR_MISALIGNED, "%s: index and sink arrays must be 4-byte aligned",
+                  who);
+  }
+  if (num_ranges < 0)
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "%s: num_ranges=%d", who, num_ranges);
+  if (!out) return fail(SINK_ATTN_ERR_NULL_ARG, "%s: out is required", who);
+  if (out_dtype != SINK_ATTN_BF16 && out_dtype != SINK_ATTN_F32)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "%s: unknown out_dtype %d", who, (int)out_dtype);
+  if (!aligned(out, 16) || (lse && !aligned(lse, 4)))
+    return fail(SINK_ATTN_ERR_MISALIGNED, "%s: out must be 16-byte and lse 4-byte aligned", who);
+  const size_t need = sink_attn_decode_balanced_workspace_size(batch, num_qo_heads, num_kv_heads,
+                                                               head_dim, max_kv_len, num_ranges);
+  if (!workspace)
+    return fail(SINK_ATTN_ERR_WORKSPACE, "%s: needs a %zu-byte workspace", who, need);
+  if (workspace_bytes < need)
+    return fail(SINK_ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu needed", who,
+                workspace_bytes, need);
+  if (!aligned(workspace, 16))
+    return fail(SINK_ATTN_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", who);
+
+  const RangePlan plan = plan_ranges(batch, num_kv_heads, max_kv_len, num_ranges);
+  a->q = static_cast<const uint16_t*>(q);
+  a->k = static_cast<const uint16_t*>(k_pages);
+  a->v = static_cast<const uint16_t*>(v_pages);
+  a->page_indptr = page_indptr;
+  a->page_indices = page_indices;
+  a->kv_len = kv_len;
+  a->sinks = sinks;
+  a->batch = batch;
+  a->hq = num_qo_heads;
+  a->hkv = num_kv_heads;
+  a->n_ranges = plan.n_ranges;
+  a->min_range_pages = plan.min_pages;
+  a->scale_log2 = sm_scale * 1.4426950408889634f;
+  a->out = out;
+  a->out_f32 = out_dtype == SINK_ATTN_F32;
+  a->lse = lse;
+  a->o_part = static_cast<float*>(workspace);
+  a->lse_part = reinterpret_cast<float*>(
+      static_cast<char*>(workspace) +
+      balanced_slots(batch, plan.n_ranges) * num_qo_heads * head_dim * sizeof(float));
+  return ok();
+}
+
+}  // namespace
+
+sink_attn_status sink_attn_decode_balanced_partial(
+    const void* q, const void* k_pages, const void* v_pages, const int32_t* page_indptr,
+    const int32_t* page_indices, const int32_t* kv_len, const float* sinks, int32_t batch,
+    int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+    int32_t max_kv_len, int32_t num_ranges, float sm_scale, void* out, sink_attn_dtype out_dtype,
+    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  sa::BalancedDecodeArgs a;
+  sink_attn_status st = balanced_setup(q, k_pages, v_pages, page_indptr, page_indices, kv_len,
+                                       sinks, batch, num_qo_heads, num_kv_heads, head_dim,
+                                       page_size, max_kv_len, num_ranges, sm_scale, out, out_dtype,
+                                       lse, workspace, workspace_bytes, 1, &a);
+  if (st != SINK_ATTN_OK) return st;
+  return hip_status(sa::launch_decode_balanced(a, num_qo_heads / num_kv_heads,
+                                               static_cast<hipStream_t>(stream)),
+                    "decode_balanced_partial launch");
+}
+
+sink_attn_status sink_attn_decode_balanced_finish(
+    const int32_t* page_indptr, const float* sinks, int32_t batch, int32_t num_qo_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t max_kv_len, int32_t num_ranges, void* out,
+    sink_attn_dtype out_dtype, float* lse, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  sa::BalancedDecodeArgs a;
+  sink_attn_status st = balanced_setup(nullptr, nullptr, nullptr, page_indptr, nullptr, nullptr,
+                                       sinks, batch, num_qo_heads, num_kv_heads, head_dim,
+                                       kPageSize, max_kv_len, num_ranges, 1.f, out, out_dtype,
+                                       lse, workspace, workspace_bytes, 2, &a);
+  if (st != SINK_ATTN_OK) return st;
+  return hip_status(sa::launch_decode_finish(a, static_cast<hipStream_t>(stream)),
+                    "decode_balanced_finish launch");
+}
+
+sink_attn_status sink_attn_decode_balanced(
+    const void* q, const void* k_pages, const void* v_pages, const int32_t* page_indptr,
+    const int32_t* page_indices, const int32_t* kv_len, const float* sinks, int32_t batch,
+    int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+    int32_t max_kv_len, int32_t num_ranges, float sm_scale, void* out, sink_attn_dtype out_dtype,
+    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  sa::BalancedDecodeArgs a;
+  sink_attn_status st = balanced_setup(q, k_pages, v_pages, page_indptr, page_indices, kv_len,
+                                       sinks, batch, num_qo_heads, num_kv_heads, head_dim,
+                                       page_size, max_kv_len, num_ranges, sm_scale, out, out_dtype,
+                                       lse, workspace, workspace_bytes, 3, &a);
+  if (st != SINK_ATTN_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(sa::launch_decode_balanced(a, num_qo_heads / num_kv_heads, s),
+                  "decode_balanced launch");
+  if (st != SINK_ATTN_OK) return st;
+  return hip_status(sa::launch_decode_finish(a, s), "decode_balanced finish launch");
 }
 
 }  // extern "C"

@@ -27,6 +27,25 @@ struct DecodeArgs {
   int32_t write_partials;       // 1: write o_part/lse_part, 0: write out/lse
 };
 
+struct BalancedDecodeArgs {
+  const uint16_t* q;            // bf16 [B, Hq, 64]
+  const uint16_t* k;            // bf16 [num_pages, Hkv, 16, 64]
+  const uint16_t* v;
+  const int32_t* page_indptr;   // [B+1]
+  const int32_t* page_indices;  // [nnz]
+  const int32_t* kv_len;        // [B]
+  const float* sinks;           // [Hq] or nullptr
+  int32_t batch, hq, hkv;
+  int32_t n_ranges;             // page ranges per KV head, a multiple of 4
+  int32_t min_range_pages;      // lower bound of the range width
+  float scale_log2;             // sm_scale * log2(e)
+  void* out;                    // [B, Hq, 64]
+  int32_t out_f32;
+  float* lse;                   // [B, Hq] or nullptr
+  float* o_part;                // [n_ranges + B - 1, Hq, 64]
+  float* lse_part;              // [n_ranges + B - 1, Hq]
+};
+
 struct MergeArgs {
   const float* o_parts;         // [N, H, S, 64]
   const float* lse_parts;       // [N, H, S] natural log
@@ -55,6 +74,8 @@ struct PrefillArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
+hipError_t launch_decode_balanced(const BalancedDecodeArgs& a, int group, hipStream_t stream);
+hipError_t launch_decode_finish(const BalancedDecodeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t stream);
 

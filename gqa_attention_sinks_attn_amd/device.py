@@ -13,7 +13,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (BF16, F32, sink_attn_decode, sink_attn_decode_num_splits,
+from . import (BF16, F32, sink_attn_decode, sink_attn_decode_balanced,
+               sink_attn_decode_balanced_workspace_size, sink_attn_decode_num_splits,
                sink_attn_decode_workspace_size, sink_attn_prefill)
 
 
@@ -44,6 +45,8 @@ class DeviceBatch:
     lse: torch.Tensor = None
     workspace: Optional[torch.Tensor] = None
     workspace_bytes: int = 0
+    plan: str = "chunked"          # decode: "chunked" (split-KV) or "balanced"
+    num_ranges: int = 0            # balanced plan: ranges per KV head, 0 = automatic
 
 
 def _bf16(a: np.ndarray, device) -> torch.Tensor:
@@ -55,8 +58,14 @@ def _i32(a, device):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(device)
 
 
-def to_device(b, device="cuda", with_lse: bool = True, out_dtype=None) -> DeviceBatch:
-    """b: a workloads.Batch (or any object with the same attributes)."""
+def to_device(b, device="cuda", with_lse: bool = True, out_dtype=None, plan: str = "chunked",
+              num_ranges: int = 0) -> DeviceBatch:
+    """b: a workloads.Batch (or any object with the same attributes).
+    plan / num_ranges select the decode entry point: "chunked" calls
+    sink_attn_decode with the batch's num_splits, "balanced" calls
+    sink_attn_decode_balanced with num_ranges."""
+    if plan not in ("chunked", "balanced"):
+        raise ValueError(plan)
     od = out_dtype if out_dtype is not None else (
         torch.float32 if getattr(b, "out_dtype", "bf16") == "f32" else torch.bfloat16)
     total_q = int(b.qo_indptr[-1])
@@ -74,13 +83,18 @@ def to_device(b, device="cuda", with_lse: bool = True, out_dtype=None) -> Device
         batch=int(len(b.qo_indptr) - 1), num_qo_heads=int(b.num_qo_heads),
         num_kv_heads=int(b.num_kv_heads), head_dim=int(b.head_dim), page_size=int(b.page_size),
         total_q=total_q, max_qlen=max_qlen, max_kv_len=max_kv_len, sm_scale=float(b.sm_scale),
-        causal=bool(b.causal), out_dtype=od, num_splits=int(getattr(b, "num_splits", 0)))
+        causal=bool(b.causal), out_dtype=od, num_splits=int(getattr(b, "num_splits", 0)),
+        plan=plan, num_ranges=int(num_ranges))
     db.out = torch.empty((total_q, db.num_qo_heads, db.head_dim), dtype=od, device=device)
     db.lse = (torch.empty((total_q, db.num_qo_heads), dtype=torch.float32, device=device)
               if with_lse else None)
-    if db.kind == "decode":
+    if db.kind == "decode" and plan == "balanced":
+        db.workspace_bytes = sink_attn_decode_balanced_workspace_size(
+            db.batch, db.num_qo_heads, db.num_kv_heads, db.head_dim, db.max_kv_len, db.num_ranges)
+    elif db.kind == "decode":
         db.workspace_bytes = sink_attn_decode_workspace_size(
             db.batch, db.num_qo_heads, db.num_kv_heads, db.head_dim, db.max_kv_len, db.num_splits)
+    if db.kind == "decode":
         db.workspace = (torch.zeros(db.workspace_bytes, dtype=torch.uint8, device=device)
                         if db.workspace_bytes else None)
     return db
@@ -99,6 +113,12 @@ def run(db: DeviceBatch, stream=None) -> None:
                           db.kv_len, db.sinks, db.batch, db.num_qo_heads, db.num_kv_heads,
                           db.head_dim, db.page_size, db.total_q, db.max_qlen, db.max_kv_len,
                           db.sm_scale, db.causal, db.out, code, db.lse, stream)
+    elif db.kind == "decode" and db.plan == "balanced":
+        sink_attn_decode_balanced(
+            db.q, db.k, db.v, db.kv_indptr, db.page_indices, db.kv_len, db.sinks, db.batch,
+            db.num_qo_heads, db.num_kv_heads, db.head_dim, db.page_size, db.max_kv_len,
+            db.num_ranges, db.sm_scale, db.out, code, db.lse, db.workspace, db.workspace_bytes,
+            stream)
     elif db.kind == "decode":
         sink_attn_decode(db.q, db.k, db.v, db.kv_indptr, db.page_indices, db.kv_len, db.sinks,
                          db.batch, db.num_qo_heads, db.num_kv_heads, db.head_dim, db.page_size,

@@ -114,19 +114,22 @@ sink_attn_status sink_attn_prefill(
     void* stream);
 
 /*
- * Number of KV splits the decode planner uses for these sizes when
- * num_splits = 0 is passed (always >= 1).  Host-only; no device access.
+ * Number of KV chunks per request of the split-KV plan for these sizes
+ * (num_splits = 0: the planner's choice, as sink_attn_decode_partial uses
+ * it; always >= 1).  Host-only; no device access.
  */
 int32_t sink_attn_decode_num_splits(int32_t batch, int32_t num_qo_heads,
                                     int32_t num_kv_heads, int32_t max_kv_len,
                                     int32_t num_splits);
 
 /*
- * Workspace bytes that sink_attn_decode needs for these sizes (0 when the
- * plan has a single split: then the kernel writes the output directly).
- * num_splits = 0 means the automatic plan.  Layout inside the workspace:
- * fp32 partial outputs [batch, Hq, S, 64] followed by fp32 partial
- * log-sum-exps [batch, Hq, S].
+ * Workspace bytes that sink_attn_decode needs for these sizes and
+ * num_splits.  num_splits = 0 (the automatic plan): when max_kv_len exceeds
+ * 16 pages the call runs the load-balanced plan and needs
+ * sink_attn_decode_balanced_workspace_size(..., num_ranges = 0) bytes;
+ * otherwise one chunk per request and 0 bytes.  num_splits = S > 0: 0 when
+ * S = 1 (the kernel writes the output directly), else fp32 partial outputs
+ * [batch, Hq, S, 64] followed by fp32 partial log-sum-exps [batch, Hq, S].
  */
 size_t sink_attn_decode_workspace_size(int32_t batch, int32_t num_qo_heads,
                                        int32_t num_kv_heads, int32_t head_dim,
@@ -144,10 +147,13 @@ size_t sink_attn_decode_workspace_size(int32_t batch, int32_t num_qo_heads,
  *                sink_attn_prefill (page_indptr = kv_indptr).
  *   max_kv_len   host upper bound of kv_len[b].
  *   num_splits   S >= 1 chunks of ceil(max_kv_len/S) keys rounded up to a
- *                multiple of 16, or 0 for the automatic plan.  Chunk 0 (keys
- *                0 ..) carries the sink; a chunk past a request's keys is
- *                empty.  S > 1 writes partials to the workspace, then merges
- *                them on the same stream.
+ *                multiple of 16.  Chunk 0 (keys 0 ..) carries the sink; a
+ *                chunk past a request's keys is empty.  S > 1 writes
+ *                partials to the workspace, then merges them on the same
+ *                stream.  0 = the automatic plan: requests of up to 16 pages
+ *                take one chunk; longer batches run sink_attn_decode_balanced
+ *                with its automatic range count (same result, work split by
+ *                pages across the whole batch).
  *   out          [batch, Hq, 64] in out_dtype;  lse fp32 [batch, Hq] or NULL.
  *   workspace    device buffer of at least sink_attn_decode_workspace_size()
  *                bytes (may be NULL when that size is 0).
@@ -208,6 +214,87 @@ sink_attn_status sink_attn_merge(
     const float* o_parts, const float* lse_parts,
     int32_t num_rows, int32_t num_heads, int32_t num_splits, int32_t head_dim,
     void* out, sink_attn_dtype out_dtype, float* lse_out,
+    void* stream);
+
+/*
+ * Load-balanced decode: the same result as sink_attn_decode, with the work
+ * cut by pages instead of by request (same section: work parallelised
+ * across heads and along the KV sequence, the sink entering once per
+ * sequence).  Per KV head the batch's pages, page_indices[0 ..
+ * page_indptr[batch]-1], are split into num_ranges equal ranges of
+ * consecutive entries, one per wave, so every wave streams the same number
+ * of pages whatever the mix of lengths.  A request that lies inside one
+ * range is finished there; the partials of a request that spans several
+ * ranges are merged by log-sum-exp in a second pass, the sink entering
+ * only the partial that holds the request's first page.
+ *
+ * Arguments as in sink_attn_decode, except:
+ *   page_indptr  rows of the page table must be non-decreasing with
+ *                page_indptr[0] = 0; a request's row may hold more pages
+ *                than ceil(kv_len[b]/16) (the extra keys are masked, but
+ *                their pages are read) and must hold at least that many.
+ *   num_ranges   ranges per KV head, rounded up to a multiple of 4, or 0 for
+ *                the automatic plan (sink_attn_decode_num_ranges()).
+ *   workspace    required: at least sink_attn_decode_balanced_workspace_size()
+ *                bytes, 16-byte aligned.  Layout: fp32 partial outputs
+ *                [num_ranges + batch - 1, Hq, 64], then fp32 partial
+ *                log-sum-exps [num_ranges + batch - 1, Hq] at the next
+ *                256-byte boundary.  Nothing needs clearing between calls;
+ *                calls that share one workspace must not overlap in time.
+ */
+int32_t sink_attn_decode_num_ranges(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len,
+                                    int32_t num_ranges);
+
+size_t sink_attn_decode_balanced_workspace_size(int32_t batch, int32_t num_qo_heads,
+                                                int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t max_kv_len, int32_t num_ranges);
+
+/* Both passes, enqueued on `stream`. */
+sink_attn_status sink_attn_decode_balanced(
+    const void* q,
+    const void* k_pages, const void* v_pages,
+    const int32_t* page_indptr, const int32_t* page_indices,
+    const int32_t* kv_len,
+    const float* sinks,
+    int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t page_size,
+    int32_t max_kv_len, int32_t num_ranges,
+    float sm_scale,
+    void* out, sink_attn_dtype out_dtype, float* lse,
+    void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/*
+ * The first pass alone: streams the pages, writes out/lse of every request
+ * that lies inside one range and the partials of the others into the
+ * workspace.  sink_attn_decode_balanced_finish with the same sizes,
+ * num_ranges, out, lse and workspace completes the call.
+ */
+sink_attn_status sink_attn_decode_balanced_partial(
+    const void* q,
+    const void* k_pages, const void* v_pages,
+    const int32_t* page_indptr, const int32_t* page_indices,
+    const int32_t* kv_len,
+    const float* sinks,
+    int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t page_size,
+    int32_t max_kv_len, int32_t num_ranges,
+    float sm_scale,
+    void* out, sink_attn_dtype out_dtype, float* lse,
+    void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/*
+ * The second pass alone: merges the partials of every request that spans
+ * several ranges and writes requests without pages (o = 0, lse = sigma or
+ * -inf).  Reads page_indptr and the workspace the first pass wrote.
+ */
+sink_attn_status sink_attn_decode_balanced_finish(
+    const int32_t* page_indptr, const float* sinks,
+    int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t max_kv_len, int32_t num_ranges,
+    void* out, sink_attn_dtype out_dtype, float* lse,
+    void* workspace, size_t workspace_bytes,
     void* stream);
 
 /* Static description of a status code. */

@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -177,3 +178,143 @@ def test_python_binding_raises_with_detail():
     with pytest.raises(sa.SinkAttnError) as e:
         sa.sink_attn_merge(None, A2, 4, 64, 8, 64, A3, 0, None, stream=0)
     assert e.value.status == NULL and "required" in e.value.detail
+
+
+# ------------------------------------------------------- load-balanced decode
+
+def call_balanced(fn="sink_attn_decode_balanced", **over):
+    a = dict(q=A, k=A, v=A, page_indptr=A, page_indices=A, kv_len=A, sinks=A, batch=64,
+             num_qo_heads=64, num_kv_heads=8, head_dim=64, page_size=16, max_kv_len=4096,
+             num_ranges=0, sm_scale=0.125, out=A2, out_dtype=1, lse=None, workspace=A3,
+             workspace_bytes=None, stream=0)
+    a.update(over)
+    if a["workspace_bytes"] is None:
+        a["workspace_bytes"] = sa.sink_attn_decode_balanced_workspace_size(
+            a["batch"], a["num_qo_heads"], a["num_kv_heads"], 64, a["max_kv_len"], a["num_ranges"])
+    f = getattr(sa.lib(), fn)
+    if fn == "sink_attn_decode_balanced_finish":
+        return f(a["page_indptr"], a["sinks"], a["batch"], a["num_qo_heads"], a["num_kv_heads"],
+                 a["head_dim"], a["max_kv_len"], a["num_ranges"], a["out"], a["out_dtype"],
+                 a["lse"], a["workspace"], a["workspace_bytes"], a["stream"])
+    return f(a["q"], a["k"], a["v"], a["page_indptr"], a["page_indices"], a["kv_len"], a["sinks"],
+             a["batch"], a["num_qo_heads"], a["num_kv_heads"], a["head_dim"], a["page_size"],
+             a["max_kv_len"], a["num_ranges"], a["sm_scale"], a["out"], a["out_dtype"], a["lse"],
+             a["workspace"], a["workspace_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("fn", ["sink_attn_decode_balanced", "sink_attn_decode_balanced_partial"])
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(page_indices=None), NULL),
+    (dict(out=None), NULL), (dict(batch=0), SHAPE), (dict(num_ranges=-4), SHAPE),
+    (dict(num_kv_heads=3), SHAPE), (dict(max_kv_len=-1), SHAPE), (dict(sm_scale=-1.0), SHAPE),
+    (dict(head_dim=128), UNSUP), (dict(page_size=32), UNSUP), (dict(out_dtype=5), UNSUP),
+    (dict(num_qo_heads=256, num_kv_heads=8), UNSUP),
+    (dict(q=A + 4), MISAL), (dict(out=A2 + 8), MISAL), (dict(page_indptr=A + 2), MISAL),
+    (dict(workspace=None), WS), (dict(workspace_bytes=1024), WS), (dict(workspace=A3 + 8), MISAL),
+])
+def test_balanced_rejects(fn, over, code):
+    assert call_balanced(fn, **over) == code
+    assert sa.sink_attn_last_error() != ""
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(page_indptr=None), NULL), (dict(out=None), NULL), (dict(batch=-1), SHAPE),
+    (dict(num_ranges=-1), SHAPE), (dict(head_dim=32), UNSUP), (dict(out_dtype=9), UNSUP),
+    (dict(workspace=None), WS), (dict(workspace_bytes=64), WS), (dict(lse=A + 2), MISAL),
+])
+def test_balanced_finish_rejects(over, code):
+    # the finish pass needs neither q nor the cache
+    assert call_balanced("sink_attn_decode_balanced_finish", q=None, k=None, v=None,
+                         **over) == code
+
+
+def test_balanced_plan_and_workspace():
+    # automatic plan: one workgroup (four ranges) per CU over all KV heads
+    assert sa.sink_attn_decode_num_ranges(64, 8, 4096, 0) == 128
+    assert sa.sink_attn_decode_num_ranges(4, 8, 131072, 0) == 128
+    assert sa.sink_attn_decode_num_ranges(4, 1, 131072, 0) == 1024
+    for hkv in (1, 2, 3, 4, 5, 8, 16, 64):
+        r = sa.sink_attn_decode_num_ranges(256, hkv, 16384, 0)
+        assert r % 4 == 0 and r >= 4 and hkv * r // 4 <= 256
+    # short batches: ranges of at least 8 pages
+    assert sa.sink_attn_decode_num_ranges(1, 8, 100, 0) == 4
+    assert sa.sink_attn_decode_num_ranges(2, 8, 16 * 64, 0) == 16
+    # explicit counts round up to a multiple of 4
+    assert sa.sink_attn_decode_num_ranges(64, 8, 4096, 5) == 8
+    assert sa.sink_attn_decode_num_ranges(64, 8, 4096, 400) == 400
+    # workspace: partials for n_ranges + batch - 1 slots, lse at the next 256-byte boundary
+    for B, R in [(64, 0), (64, 12), (1, 0), (4500, 100)]:
+        n = sa.sink_attn_decode_num_ranges(B, 2, 4096, R)
+        rows = (n + B - 1) * 16
+        assert sa.sink_attn_decode_balanced_workspace_size(B, 16, 2, 64, 4096, R) == \
+            rows * 64 * 4 + ((rows * 4 + 255) // 256) * 256
+
+
+def test_decode_automatic_plan_uses_the_balanced_workspace():
+    # more than 16 pages per request: the balanced plan and its workspace
+    assert sa.sink_attn_decode_workspace_size(64, 64, 8, 64, 4096, 0) == \
+        sa.sink_attn_decode_balanced_workspace_size(64, 64, 8, 64, 4096, 0)
+    need = sa.sink_attn_decode_workspace_size(64, 64, 8, 64, 4096, 0)
+    assert call_decode(batch=64, max_kv_len=4096, num_splits=0, workspace=None,
+                       workspace_bytes=0) == WS
+    assert call_decode(batch=64, max_kv_len=4096, num_splits=0, workspace_bytes=need - 1) == WS
+    # up to 16 pages: one chunk, no workspace
+    assert sa.sink_attn_decode_workspace_size(64, 64, 8, 64, 256, 0) == 0
+
+
+def _simulate_partition(indptr, n_ranges, min_pages):
+    """Host model of the page partition of the balanced decode: the ranges,
+    the segments each range's wave closes (request, first page, sink?, slot
+    or direct), and the slots the finish pass reads per request."""
+    B = len(indptr) - 1
+    nnz = indptr[-1]
+    Rw = max(min_pages, -(-nnz // n_ranges))
+    owner = np.repeat(np.arange(B), np.diff(indptr))
+    segs = []
+    for u in range(n_ranges):
+        p0, p1 = u * Rw, min(nnz, u * Rw + Rw)
+        pg = p0
+        while pg < p1:
+            b = owner[pg]
+            end = min(p1, indptr[b + 1])
+            whole = indptr[b] // Rw == (indptr[b + 1] - 1) // Rw
+            segs.append((u, b, pg, end, pg == indptr[b], None if whole else u + b))
+            pg = end
+    reads = {}
+    for b in range(B):
+        if indptr[b + 1] > indptr[b]:
+            u0, u1 = indptr[b] // Rw, (indptr[b + 1] - 1) // Rw
+            if u0 != u1:
+                reads[b] = [u + b for u in range(u0, u1 + 1)]
+    return Rw, segs, reads
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_balanced_partition_covers_every_page_once(seed):
+    """Every page is streamed by exactly one wave; each request gets the sink
+    exactly once (in the segment holding its first page); partial slots are
+    unique and within the workspace; the finish pass reads exactly the slots
+    the first pass wrote for the request."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 300))
+    pages = rng.integers(0, 40, size=B)
+    pages[rng.random(B) < 0.2] = 0
+    indptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.int64)
+    for R in (4, 8, 12, 100):
+        n = sa.sink_attn_decode_num_ranges(B, 2, 40 * 16, R)
+        Rw, segs, reads = _simulate_partition(indptr, n, 1)
+        assert Rw * n >= indptr[-1]
+        seen = np.zeros(int(indptr[-1]), np.int64)
+        sinks = np.zeros(B, np.int64)
+        slots = {}
+        for u, b, s0, s1, has_sink, slot in segs:
+            seen[s0:s1] += 1
+            sinks[b] += has_sink
+            if slot is not None:
+                assert slot not in slots and 0 <= slot < n + B - 1
+                slots[slot] = b
+        assert np.all(seen == 1)
+        assert np.array_equal(sinks, (pages > 0).astype(np.int64))
+        for b, rs in reads.items():
+            assert all(slots.get(s) == b for s in rs)
+        assert sorted(slots) == sorted(s for rs in reads.values() for s in rs)
