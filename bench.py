@@ -52,8 +52,8 @@ KV_COPIES = 4                  # rotated KV pools: 4 x 269 MB > 256 MB last-leve
 # (python bench.py --mode traffic), each scaled by the same counter on a
 # 256 MiB copy; see profiles/.  Valid for the kernel sources they were taken
 # on -- reset to None whenever decode_balanced.hip or prefill.hip changes.
-DECODE_TRAFFIC_BYTES = 260_966_351
-PREFILL_TRAFFIC_BYTES = 1_362_741_767
+DECODE_TRAFFIC_BYTES = 260_941_603
+PREFILL_TRAFFIC_BYTES = 1_896_629_683
 
 
 def log(msg: str):

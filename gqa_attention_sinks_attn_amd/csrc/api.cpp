@@ -228,6 +228,14 @@ sink_attn_status sink_attn_prefill(const void* q, const int32_t* qo_indptr, cons
       (kv_len && !aligned(kv_len, 4)) || (sinks && !aligned(sinks, 4)) || (lse && !aligned(lse, 4)))
     return fail(SINK_ATTN_ERR_MISALIGNED, "prefill: index, sink and lse arrays must be 4-byte aligned");
   if (total_q == 0 || max_qlen == 0) return ok();
+  {
+    // one workgroup per (256 / G query tokens, KV head, request): a flat grid
+    const int64_t tokens_per_wg = 256 / (num_qo_heads / num_kv_heads);
+    const int64_t wgs = (max_qlen + tokens_per_wg - 1) / tokens_per_wg * num_kv_heads * (int64_t)batch;
+    if (wgs > 0x7fffffff)
+      return fail(SINK_ATTN_ERR_BAD_SHAPE, "prefill: %lld workgroups exceed the grid limit",
+                  (long long)wgs);
+  }
 
   sa::PrefillArgs a;
   a.q = static_cast<const uint16_t*>(q);

@@ -13,6 +13,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Work-item and workgroup indices read straight from the hardware registers
+// (the runtime's accessor functions are not inlined into kernels built
+// without IEEE mode, and would cost a call at every kernel start).
+__device__ __forceinline__ int thread_x() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int block_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int block_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
+__device__ __forceinline__ int block_z() { return (int)__builtin_amdgcn_workgroup_id_z(); }
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kWave = 64;

@@ -65,14 +65,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kLdsBytes];
   uint16_t* lds_v = reinterpret_cast<uint16_t*>(lds_raw);
 
-  const int unit = blockIdx.x;          // b * Hkv + g
-  const int c = blockIdx.y;             // chunk
+  const int unit = block_x();          // b * Hkv + g
+  const int c = block_y();             // chunk
   const int g = unit % p.hkv;
   const int b = unit / p.hkv;
-  const int lane = threadIdx.x & 63;
+  const int lane = thread_x() & 63;
   // wave index in an SGPR: everything derived from it (page ranges, page-id
   // addresses) stays scalar, so page ids come through scalar loads
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(thread_x() >> 6);
   const int col = lane & 15;     // head column of the MFMA tile
   const int grp = lane >> 4;     // lane group 0..3
   const bool live_col = col < G;
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
   __syncthreads();
 
   // 256 threads: column t / 16, dims 4 (t % 16) .. +3
-  const int t = threadIdx.x;
+  const int t = thread_x();
   const int oc = t >> 4;
   const int d0 = 4 * (t & 15);
   if (oc >= G) return;

@@ -90,10 +90,10 @@ template <int G>
 __global__ __launch_bounds__(256) void decode_balanced_kernel(BalancedDecodeArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[kWaves * kWaveLds];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = blockIdx.y;
-  const int u = blockIdx.x * kWaves + wave;   // this wave's range
+  const int lane = thread_x() & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(thread_x() >> 6);
+  const int g = block_y();
+  const int u = block_x() * kWaves + wave;   // this wave's range
   const int col = lane & 15;
   const int grp = lane >> 4;
   const bool live_col = col < G;
@@ -396,8 +396,8 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(BalancedDecodeArgs
 // pages.  All loads of one (request, head) go out together: the lse values
 // lane-parallel, the first eight partial rows unconditionally.
 __global__ __launch_bounds__(256) void decode_finish_kernel(BalancedDecodeArgs p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t pair = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = thread_x() & 63;
+  const int64_t pair = (int64_t)block_x() * 4 + __builtin_amdgcn_readfirstlane(thread_x() >> 6);
   if (pair >= (int64_t)p.batch * p.hq) return;
   const int b = (int)(pair / p.hq);
   const int h = (int)(pair % p.hq);

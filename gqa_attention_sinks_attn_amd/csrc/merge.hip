@@ -18,8 +18,8 @@ namespace {
 constexpr int kD = 64;
 
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = thread_x() & 63;
+  const int64_t pair = (int64_t)block_x() * 4 + (thread_x() >> 6);
   const int64_t n_pairs = (int64_t)p.rows * p.heads;
   if (pair >= n_pairs) return;
   const int S = p.splits;

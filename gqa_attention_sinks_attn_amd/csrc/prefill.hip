@@ -31,7 +31,11 @@
 //     transposed with ds_read_b64_tr_b16 in the key order of the score
 //     layout;
 //   * masking (causal edge, ragged tail) is applied only on tiles that
-//     straddle an edge; late query tiles are launched first.
+//     straddle an edge, comparing key offsets inside the tile (constants)
+//     against one per-row limit;
+//   * the grid is flat with the query tile as its slowest index, so the
+//     longest query tiles of every (request, KV head) pair start first and
+//     the short ones fill the tail.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -69,9 +73,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * kKBuf];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * kVBuf];
 
-  const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;  // late (long) tiles first
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  // globally longest first: the grid is flat, the q tile is the slowest index
+  const int q_tiles = (p.max_qlen + T - 1) / T;
+  const int units = p.hkv * p.batch;
+  const int wg = block_x();
+  const int qt = q_tiles - 1 - wg / units;
+  const int g = (wg % units) % p.hkv;
+  const int b = (wg % units) / p.hkv;
   const int q_begin = p.qo_indptr[b];
   const int qlen = p.qo_indptr[b + 1] - q_begin;
   const int t0 = qt * T;
@@ -82,7 +90,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   else L = p.kv_indptr[b + 1] - kv_start;
   const int pos_base = L - qlen;  // absolute position of token 0
 
-  const int tid = threadIdx.x;
+  const int tid = thread_x();
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int r = lane & 31;
@@ -199,16 +207,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       uint32_t pk[2][2][2][4];  // [cb][kb][half][pair]
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const int lim = !edge ? 0x7fffffff : (p.causal ? min(pos[cb], L - 1) : L - 1);
         auto mask = [&]() {
           if (edge) {
+            const int lim = p.causal ? min(pos[cb], L - 1) : L - 1;
+            const int rel = lim - key0 - 4 * hh;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int j = 0; j < 16; ++j) {
-                const int key = key0 + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
-                if (key > lim) sacc[kb][cb][j] = -INFINITY;
-              }
+              for (int j = 0; j < 16; ++j)
+                if (32 * kb + 8 * (j >> 2) + (j & 3) > rel) sacc[kb][cb][j] = -INFINITY;
           }
         };
         mask();
@@ -325,7 +332,9 @@ hipError_t launch_g(const PrefillArgs& a, hipStream_t stream) {
   constexpr int T = 256 / G;
   const int q_tiles = (a.max_qlen + T - 1) / T;
   if (q_tiles == 0 || a.batch == 0) return hipSuccess;
-  dim3 grid(q_tiles, a.hkv, a.batch);
+  const int64_t wgs = (int64_t)q_tiles * a.hkv * a.batch;
+  if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)wgs);
   if (a.page_indices != nullptr)
     hipLaunchKernelGGL((prefill_kernel<G, true>), grid, dim3(256), 0, stream, a);
   else
