@@ -53,7 +53,7 @@ KV_COPIES = 4                  # rotated KV pools: 4 x 269 MB > 256 MB last-leve
 # 256 MiB copy; see profiles/.  Valid for the kernel sources they were taken
 # on -- reset to None whenever decode_balanced.hip or prefill.hip changes.
 DECODE_TRAFFIC_BYTES = 260_941_603
-PREFILL_TRAFFIC_BYTES = 1_896_629_683
+PREFILL_TRAFFIC_BYTES = 1_879_085_767
 
 
 def log(msg: str):

@@ -146,31 +146,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int ld_row = tid >> 3;   // 0..31
   const int ld_chunk = tid & 7;  // 16-byte chunk within a 128-byte row
   u32x4 rk0, rk1, rv0, rv1;
+  // Loads are unconditional (no branch, so the compiler's waits stay
+  // exact): tiles past the last one are clamped to it, and rows past the
+  // last key read row 0 of the request.  Their scores are masked (every tile
+  // holding such rows is an edge tile), and their V rows are zeroed when
+  // stored (their weight is 0, and 0 x garbage must stay 0).
+  const int64_t vdelta = p.v - p.k;
+  auto tile_key0 = [&](int kt) { return min(kt, n_tiles - 1) * kTile; };
   auto load_tile = [&](int kt) {
-    const int key0 = kt * kTile;
-    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int key0 = tile_key0(kt);
     const int ka = key0 + ld_row, kb2 = key0 + 32 + ld_row;
     const uint16_t* pa = kv_row<PAGED>(p, p.k, g, ka < L ? ka : 0, kv_start) + 8 * ld_chunk;
     const uint16_t* pb = kv_row<PAGED>(p, p.k, g, kb2 < L ? kb2 : 0, kv_start) + 8 * ld_chunk;
-    const int64_t vdelta = p.v - p.k;
-    rk0 = ka < L ? ld16(pa) : z;
-    rk1 = kb2 < L ? ld16(pb) : z;
-    // V rows past the last key are zero (their weight is 0; 0 x garbage must stay 0)
-    rv0 = ka < L ? ld16(pa + vdelta) : z;
-    rv1 = kb2 < L ? ld16(pb + vdelta) : z;
+    rk0 = ld16(pa);
+    rk1 = ld16(pb);
+    rv0 = ld16(pa + vdelta);
+    rv1 = ld16(pb + vdelta);
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, int kt) {
+    const int key0 = tile_key0(kt);
+    const u32x4 z = {0u, 0u, 0u, 0u};
     uint16_t* kd = lds_k + buf * kKBuf;
     uint16_t* vd = lds_v + buf * kVBuf;
     *reinterpret_cast<u32x4*>(kd + ld_row * kKPitch + 8 * ld_chunk) = rk0;
     *reinterpret_cast<u32x4*>(kd + (32 + ld_row) * kKPitch + 8 * ld_chunk) = rk1;
-    *reinterpret_cast<u32x4*>(vd + ld_row * kVPitch + 8 * ld_chunk) = rv0;
-    *reinterpret_cast<u32x4*>(vd + (32 + ld_row) * kVPitch + 8 * ld_chunk) = rv1;
+    *reinterpret_cast<u32x4*>(vd + ld_row * kVPitch + 8 * ld_chunk) = key0 + ld_row < L ? rv0 : z;
+    *reinterpret_cast<u32x4*>(vd + (32 + ld_row) * kVPitch + 8 * ld_chunk) =
+        key0 + 32 + ld_row < L ? rv1 : z;
   };
 
   if (n_tiles > 0) {
     load_tile(0);
-    store_tile(0);
+    store_tile(0, 0);
   }
   __syncthreads();
 
@@ -182,82 +189,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < n_tiles) load_tile(kt + 1);
+    load_tile(kt + 1);   // clamped: the last iteration repeats the last tile
     const int key0 = kt * kTile;
     const bool wave_live = !p.causal || key0 <= wave_pos_max;
     if (wave_live) {
       const uint16_t* kbuf = lds_k + buf * kKBuf;
       const uint16_t* vbuf = lds_v + buf * kVBuf;
+      const bool edge = (p.causal && key0 + kTile - 1 > pos_min_wg) || (key0 + kTile > L);
+      const f32x16 zero16 = {};
+      // K operand (A of S^T) for k-step s, key block kb: keys 32 kb + r,
+      // dims 16 s + 8 hh.  V^T operand (A of O^T) for key block kb, half hf,
+      // dim block db: dims 32 db + .., keys 32 kb + 16 hf + {4 hh .., 8 + 4 hh ..}.
+      auto kop = [&](int s, int kb) {
+        return as_bf16x8(*reinterpret_cast<const u32x4*>(kbuf + (32 * kb + r) * kKPitch + 16 * s + 8 * hh));
+      };
+      auto vop = [&](int kb, int hf, int db) {
+        const uint16_t* src = vbuf + (32 * kb + 16 * hf + tr_row) * kVPitch + tr_col + 32 * db;
+        return as_bf16x8(lds_tr16_pair(src, src + 8 * kVPitch));
+      };
       // S^T[kb][cb]: keys 32 kb + 8 (j/4) + 4 hh + j%4, column = row r of cb
       f32x16 sacc[2][2];
-      const f32x16 zero16 = {};
+      uint32_t pk[2][2][2][4];  // [cb][kb][hf][pair]
+      auto mask = [&](int cb) {
+        const int lim = p.causal ? min(pos[cb], L - 1) : L - 1;
+        int rel = lim - key0 - 4 * hh;
+        // defined here, so the compares below cannot be hoisted out of the
+        // (rare) edge branch into every tile
+        asm volatile("" : "+v"(rel));
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 a0 = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(kbuf + r * kKPitch + 16 * s + 8 * hh));
-        const bf16x8 a1 = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(kbuf + (32 + r) * kKPitch + 16 * s + 8 * hh));
-        sacc[0][0] = mfma32(a0, bq[0][s], s == 0 ? zero16 : sacc[0][0]);
-        sacc[1][0] = mfma32(a1, bq[0][s], s == 0 ? zero16 : sacc[1][0]);
-        sacc[0][1] = mfma32(a0, bq[1][s], s == 0 ? zero16 : sacc[0][1]);
-        sacc[1][1] = mfma32(a1, bq[1][s], s == 0 ? zero16 : sacc[1][1]);
-      }
-
-      const bool edge = (p.causal && key0 + kTile - 1 > pos_min_wg) || (key0 + kTile > L);
-      uint32_t pk[2][2][2][4];  // [cb][kb][half][pair]
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        auto mask = [&]() {
-          if (edge) {
-            const int lim = p.causal ? min(pos[cb], L - 1) : L - 1;
-            const int rel = lim - key0 - 4 * hh;
+          for (int j = 0; j < 16; ++j)
+            if (32 * kb + 8 * (j >> 2) + (j & 3) > rel) sacc[kb][cb][j] = -INFINITY;
+      };
+      // exp2(s * scale - m) of the scores j = 8 hf + 2 q, +1 (q = 2 qp, 2 qp + 1)
+      // of key block kb, packed; the row sum adds the rounded values the MFMA
+      // consumes (v_dot2 with 1.0 accumulates in fp32), so every row stays an
+      // exact convex combination of V.
+      auto expo4 = [&](int cb, float neg_m, int kb, int hf, int qp, float& acc) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int j = 0; j < 16; ++j)
-                if (32 * kb + 8 * (j >> 2) + (j & 3) > rel) sacc[kb][cb][j] = -INFINITY;
-          }
-        };
-        mask();
-        // Fast path: exponentiate against the current reference m.  It is
-        // valid while every p stays below 2^15 and the row has a reference;
-        // otherwise (rare: a new maximum, or the row's first live tile
-        // without a sink) the tile's scores are recomputed, the true row
-        // maximum taken, and O, d and m rescaled before exponentiating.
-        // exponentiate and pack: slot pair q of half hf <-> S^T entries
-        // j = 8 hf + 2 q, 8 hf + 2 q + 1 of key block kb
-        auto expo = [&](float neg_m) {
-          float acc = 0.f;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const int j = 8 * hf + 2 * q;
-                const float e0 = fast_exp2(__builtin_fmaf(sacc[kb][cb][j], sl2, neg_m));
-                const float e1 = fast_exp2(__builtin_fmaf(sacc[kb][cb][j + 1], sl2, neg_m));
-                const uint32_t w = pack_bf16x2(e0, e1);
-                pk[cb][kb][hf][q] = w;
-                // sum the rounded values the MFMA consumes (v_dot2 with 1.0
-                // accumulates in fp32), so every row stays an exact convex
-                // combination of V
-                acc = dot2_sum(w, acc);
-              }
-          return acc;
-        };
-        float ds = expo((m[cb] == -INFINITY) ? 0.f : -m[cb]);
+        for (int q = 2 * qp; q < 2 * qp + 2; ++q) {
+          const int j = 8 * hf + 2 * q;
+          const float e0 = fast_exp2(__builtin_fmaf(sacc[kb][cb][j], sl2, neg_m));
+          const float e1 = fast_exp2(__builtin_fmaf(sacc[kb][cb][j + 1], sl2, neg_m));
+          const uint32_t w = pack_bf16x2(e0, e1);
+          pk[cb][kb][hf][q] = w;
+          acc = dot2_sum(w, acc);
+        }
+      };
+      auto neg_ref = [&](int cb) { return (m[cb] == -INFINITY) ? 0.f : -m[cb]; };
+      // Fast path: the tile was exponentiated against the current reference
+      // m.  It is valid while every p stays below 2^15 and the row has a
+      // reference; otherwise (rare: a new maximum, or the row's first live
+      // tile without a sink) take the true row maximum, rescale O, d and m,
+      // and exponentiate again.
+      auto settle_row = [&](int cb, float ds) {
         if (__any(!(ds <= kFastLimit) || m[cb] == -INFINITY)) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const bf16x8 a0 = as_bf16x8(
-                *reinterpret_cast<const u32x4*>(kbuf + r * kKPitch + 16 * s + 8 * hh));
-            const bf16x8 a1 = as_bf16x8(
-                *reinterpret_cast<const u32x4*>(kbuf + (32 + r) * kKPitch + 16 * s + 8 * hh));
-            sacc[0][cb] = mfma32(a0, bq[cb][s], s == 0 ? zero16 : sacc[0][cb]);
-            sacc[1][cb] = mfma32(a1, bq[cb][s], s == 0 ? zero16 : sacc[1][cb]);
-          }
-          mask();
           float mx = -INFINITY;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
@@ -271,30 +258,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           o[cb][0] *= alpha;
           o[cb][1] *= alpha;
           m[cb] = m_new;
-          ds = expo((m_new == -INFINITY) ? 0.f : -m_new);
+          float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) expo4(cb, neg_ref(cb), i >> 2, (i >> 1) & 1, i & 1, (i & 1) ? a1 : a0);
+          ds = a0 + a1;
         }
         d[cb] += ds;
-      }
+      };
+      auto pb_of = [&](int cb, int kb, int hf) {
+        return as_bf16x8(u32x4{pk[cb][kb][hf][0], pk[cb][kb][hf][1], pk[cb][kb][hf][2], pk[cb][kb][hf][3]});
+      };
 
-      // O^T[cb][db] += V^T[dims 32 db.., keys] P^T
+      // (1) S^T of column block 0.  The tile's K operands are read once and
+      //     serve both blocks.
+      bf16x8 ko[4][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const bf16x8 p0 = as_bf16x8(u32x4{pk[0][kb][hf][0], pk[0][kb][hf][1],
-                                            pk[0][kb][hf][2], pk[0][kb][hf][3]});
-          const bf16x8 p1 = as_bf16x8(u32x4{pk[1][kb][hf][0], pk[1][kb][hf][1],
-                                            pk[1][kb][hf][2], pk[1][kb][hf][3]});
-          const uint16_t* src = vbuf + (32 * kb + 16 * hf + tr_row) * kVPitch + tr_col;
+        for (int kb = 0; kb < 2; ++kb) ko[s][kb] = kop(s, kb);
 #pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            const bf16x8 a = as_bf16x8(lds_tr16_pair(src + 32 * db, src + 8 * kVPitch + 32 * db));
-            o[0][db] = mfma32(a, p0, o[0][db]);
-            o[1][db] = mfma32(a, p1, o[1][db]);
-          }
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          sacc[kb][0] = mfma32(ko[s][kb], bq[0][s], s == 0 ? zero16 : sacc[kb][0]);
+      if (edge) mask(0);
+      // (2) S^T of column block 1 on the matrix core while the vector unit
+      //     exponentiates block 0: one MFMA, then six VALU instructions.
+      {
+        float a0 = 0.f, a1 = 0.f;
+        const float nm = neg_ref(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int s = i >> 1, kb = i & 1;
+          sacc[kb][1] = mfma32(ko[s][kb], bq[1][s], s == 0 ? zero16 : sacc[kb][1]);
+          expo4(0, nm, i >> 2, (i >> 1) & 1, i & 1, (i & 1) ? a1 : a0);
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+        }
+        settle_row(0, a0 + a1);
+      }
+      if (edge) mask(1);
+      // (3) O^T of block 0 += V^T P^T on the matrix core while block 1 is
+      //     exponentiated.  The tile's V^T operands are read once, all at
+      //     the start (the first exponentials cover their latency), and
+      //     serve both blocks.
+      bf16x8 vo[2][2][2];
+      {
+        float a0 = 0.f, a1 = 0.f;
+        const float nm = neg_ref(1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vo[i >> 2][(i >> 1) & 1][i & 1] = vop(i >> 2, (i >> 1) & 1, i & 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int kb = i >> 2, hf = (i >> 1) & 1, db = i & 1;
+          o[0][db] = mfma32(vo[kb][hf][db], pb_of(0, kb, hf), o[0][db]);
+          expo4(1, nm, i >> 2, (i >> 1) & 1, i & 1, (i & 1) ? a1 : a0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);    // DS read: all of V^T
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);    // VALU
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
+        }
+        settle_row(1, a0 + a1);
+      }
+      // (4) O^T of block 1.
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kb = i >> 2, hf = (i >> 1) & 1, db = i & 1;
+        o[1][db] = mfma32(vo[kb][hf][db], pb_of(1, kb, hf), o[1][db]);
+      }
     }
-    if (kt + 1 < n_tiles) store_tile(buf ^ 1);
+    store_tile(buf ^ 1, kt + 1);
     __syncthreads();
   }
 
