@@ -149,6 +149,71 @@ def bench_decode(args, torch, sa, device, W):
     return res
 
 
+def _time_calls(torch, fn, steps, warmup):
+    """Mean ms of fn(i) over `steps` calls, HIP events on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        fn(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(c) for a, c in evs]))
+
+
+def kv_bytes_of(b) -> int:
+    return int(b.kv_len.astype(np.int64).sum()) * 2 * b.num_kv_heads * b.head_dim * 2
+
+
+def bench_extra(args, torch, sa, device, W):
+    """The other workloads, each timed whole (all kernels of the call), HIP
+    events: the long split decode (workload 3), both calls of the mixed batch
+    (workload 5), and a multi-token verification batch (64 requests, 4
+    drafted tokens each, KV lengths U[4, 4096], through sink_attn_prefill)."""
+    res = {}
+    steps, warm = max(5, min(args.steps, 20)), max(1, args.warmup)
+
+    def decode_line(name, b):
+        db = device.to_device(b, plan="balanced")
+        ms = _time_calls(torch, lambda i: device.run(db), steps, warm)
+        gbs = kv_bytes_of(b) / (ms * 1e-3) / 1e9
+        alg = decode_algorithmic_bytes(b) / (ms * 1e-3) / 1e9
+        res[name] = dict(workload=b.name, call="sink_attn_decode (automatic plan: balanced)",
+                         ms_per_call=round(ms, 5), kv_gbs=round(gbs, 1),
+                         frac_hbm=round(alg / HBM_PEAK_GBS, 4))
+        del db
+        torch.cuda.empty_cache()
+
+    def prefill_line(name, b, call="sink_attn_prefill"):
+        db = device.to_device(b, with_lse=False)
+        ms = _time_calls(torch, lambda i: device.run(db), steps, warm)
+        flops = prefill_pairs(b) * 4 * b.head_dim
+        tfs = flops / (ms * 1e-3) / 1e12
+        res[name] = dict(workload=b.name, call=call, ms_per_call=round(ms, 5),
+                         tflops=round(tfs, 2), frac_mfma=round(tfs / BF16_PEAK_TFLOPS, 4),
+                         kv_gbs=round(kv_bytes_of(b) / (ms * 1e-3) / 1e9, 1))
+        del db
+        torch.cuda.empty_cache()
+
+    log("[bench] extra: workload 3")
+    decode_line("c3_split_decode", W.config(3))
+    log("[bench] extra: workload 5")
+    mx = W.config(5)
+    prefill_line("c5_prefill", mx.prefill)
+    decode_line("c5_decode", mx.decode)
+    del mx
+    log("[bench] extra: verification batch")
+    rng = np.random.default_rng(1090)
+    L = rng.integers(4, 4096, size=64, endpoint=True)
+    vb = W.make_batch(rng, kind="prefill", qlens=[4] * 64, kv_lens=L, hq=64, hkv=8, paged=True,
+                      sinks="normal", name="verify: B=64 x 4 drafted tokens, L~U[4,4096], 64q/8kv, page 16")
+    prefill_line("verify_4tok", vb, call="sink_attn_prefill (qlen 4 per request)")
+    return res
+
+
 def bench_prefill(args, torch, sa, device, W):
     b = W.config(4)
     db = device.to_device(b, with_lse=False)
@@ -226,6 +291,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time workloads 3 and 5 and a verification batch (adds ~2 min)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--mode", choices=["bench", "traffic"], default="bench")
@@ -299,6 +366,8 @@ def main():
     }
     if pre is not None:
         line["prefill"] = pre
+    if args.extra:
+        line["extra"] = bench_extra(args, torch, sa, device, W)
     print(json.dumps(line), flush=True)
 
 
