@@ -65,7 +65,7 @@ def decode_algorithmic_bytes(b) -> int:
     (2 * Hkv * D * 2 B each), the queries, page ids and per-request lengths."""
     L = b.kv_len.astype(np.int64)
     kv = int(L.sum()) * 2 * b.num_kv_heads * b.head_dim * 2
-    q = b.batch * b.num_qo_heads * b.head_dim * 2
+    q = int(b.qo_indptr[-1]) * b.num_qo_heads * b.head_dim * 2   # query rows
     pages = int(((L + b.page_size - 1) // b.page_size).sum()) * 4
     return kv + q + pages + b.batch * 8
 
@@ -210,7 +210,16 @@ def bench_extra(args, torch, sa, device, W):
     L = rng.integers(4, 4096, size=64, endpoint=True)
     vb = W.make_batch(rng, kind="prefill", qlens=[4] * 64, kv_lens=L, hq=64, hkv=8, paged=True,
                       sinks="normal", name="verify: B=64 x 4 drafted tokens, L~U[4,4096], 64q/8kv, page 16")
-    prefill_line("verify_4tok", vb, call="sink_attn_prefill (qlen 4 per request)")
+    prefill_line("verify_4tok_prefill", vb, call="sink_attn_prefill (qlen 4 per request)")
+    db = device.to_device(vb, with_lse=False, plan="verify")
+    ms = _time_calls(torch, lambda i: device.run(db), steps, warm)
+    flops = prefill_pairs(vb) * 4 * vb.head_dim
+    res["verify_4tok"] = dict(
+        workload=vb.name, call="sink_attn_verify (automatic split plan)", ms_per_call=round(ms, 5),
+        kv_gbs=round(kv_bytes_of(vb) / (ms * 1e-3) / 1e9, 1),
+        frac_hbm=round(decode_algorithmic_bytes(vb) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        tflops=round(flops / (ms * 1e-3) / 1e12, 2))
+    del db
     return res
 
 

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsink_attn.so")
-SOURCES = ["api.cpp", "decode.hip", "decode_balanced.hip", "merge.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "decode.hip", "decode_balanced.hip", "merge.hip", "prefill.hip", "verify.hip"]
 ARCH = "gfx950"
 
 

@@ -564,4 +564,111 @@ sink_attn_status sink_attn_decode_balanced(
   return hip_status(sa::launch_decode_finish(a, s), "decode_balanced finish launch");
 }
 
+namespace {
+
+// Largest draft per request the verification kernel packs: qlen x G
+// (token, head) rows in at most four 16-column blocks.
+constexpr int32_t kVerifyMaxRows = 64;
+
+size_t verify_workspace(int32_t total_q, int32_t num_qo_heads, int32_t head_dim, int32_t splits) {
+  if (splits <= 1 || total_q <= 0) return 0;
+  const size_t rows = (size_t)total_q * num_qo_heads * splits;
+  return rows * head_dim * sizeof(float) + ((rows * sizeof(float) + 255) / 256) * 256;
+}
+
+}  // namespace
+
+size_t sink_attn_verify_workspace_size(int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t total_q, int32_t max_kv_len,
+                                       int32_t num_splits) {
+  if (batch <= 0 || num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || total_q < 0 ||
+      max_kv_len < 0 || num_splits < 0)
+    return 0;
+  return verify_workspace(total_q, num_qo_heads, head_dim,
+                          plan_splits(batch, num_kv_heads, max_kv_len, num_splits));
+}
+
+sink_attn_status sink_attn_verify(const void* q, const int32_t* qo_indptr, const void* k_pages,
+                                  const void* v_pages, const int32_t* page_indptr,
+                                  const int32_t* page_indices, const int32_t* kv_len,
+                                  const float* sinks, int32_t batch, int32_t num_qo_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                  int32_t total_q, int32_t max_qlen, int32_t max_kv_len,
+                                  int32_t num_splits, float sm_scale, void* out,
+                                  sink_attn_dtype out_dtype, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  sink_attn_status st = check_decode_common(q, k_pages, v_pages, page_indptr, page_indices, kv_len,
+                                            sinks, batch, num_qo_heads, num_kv_heads, head_dim,
+                                            page_size, max_kv_len, num_splits, sm_scale);
+  if (st != SINK_ATTN_OK) return st;
+  if (!qo_indptr || !out)
+    return fail(SINK_ATTN_ERR_NULL_ARG, "verify: qo_indptr and out are required");
+  if (total_q < 0 || max_qlen < 0 || max_qlen > total_q)
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "verify: total_q=%d max_qlen=%d", total_q, max_qlen);
+  const int32_t G = num_qo_heads / num_kv_heads;
+  if ((int64_t)max_qlen * G > kVerifyMaxRows)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED,
+                "verify: max_qlen x G = %d x %d rows exceeds %d (use sink_attn_prefill)", max_qlen,
+                G, kVerifyMaxRows);
+  if (out_dtype != SINK_ATTN_BF16 && out_dtype != SINK_ATTN_F32)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "verify: unknown out_dtype %d", (int)out_dtype);
+  if (!aligned(out, 16) || (lse && !aligned(lse, 4)) || !aligned(qo_indptr, 4))
+    return fail(SINK_ATTN_ERR_MISALIGNED,
+                "verify: out must be 16-byte, lse and qo_indptr 4-byte aligned");
+  const int32_t S = plan_splits(batch, num_kv_heads, max_kv_len, num_splits);
+  const size_t need = verify_workspace(total_q, num_qo_heads, head_dim, S);
+  if (need > 0) {
+    if (!workspace)
+      return fail(SINK_ATTN_ERR_WORKSPACE, "verify: %d splits need a %zu-byte workspace", S, need);
+    if (workspace_bytes < need)
+      return fail(SINK_ATTN_ERR_WORKSPACE, "verify: workspace of %zu bytes < %zu needed",
+                  workspace_bytes, need);
+    if (!aligned(workspace, 16))
+      return fail(SINK_ATTN_ERR_MISALIGNED, "verify: workspace must be 16-byte aligned");
+  }
+  if (total_q == 0 || max_qlen == 0) return ok();
+
+  sa::VerifyArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.qo_indptr = qo_indptr;
+  a.k = static_cast<const uint16_t*>(k_pages);
+  a.v = static_cast<const uint16_t*>(v_pages);
+  a.page_indptr = page_indptr;
+  a.page_indices = page_indices;
+  a.kv_len = kv_len;
+  a.sinks = sinks;
+  a.batch = batch;
+  a.hq = num_qo_heads;
+  a.hkv = num_kv_heads;
+  a.num_splits = S;
+  a.chunk_pages = chunk_pages_for(max_kv_len, S);
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.out = out;
+  a.out_f32 = out_dtype == SINK_ATTN_F32;
+  a.lse = lse;
+  a.o_part = nullptr;
+  a.lse_part = nullptr;
+  a.write_partials = 0;
+  if (S > 1) {
+    a.o_part = static_cast<float*>(workspace);
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          (size_t)total_q * num_qo_heads * S * head_dim * sizeof(float));
+    a.write_partials = 1;
+  }
+  const int column_blocks = (max_qlen * G + 15) / 16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(sa::launch_verify(a, G, column_blocks, s), "verify launch");
+  if (st != SINK_ATTN_OK || S == 1) return st;
+  sa::MergeArgs mg;
+  mg.o_parts = a.o_part;
+  mg.lse_parts = a.lse_part;
+  mg.rows = total_q;
+  mg.heads = num_qo_heads;
+  mg.splits = S;
+  mg.out = out;
+  mg.out_f32 = a.out_f32;
+  mg.lse = lse;
+  return hip_status(sa::launch_merge(mg, s), "verify merge launch");
+}
+
 }  // extern "C"

@@ -46,6 +46,27 @@ struct BalancedDecodeArgs {
   float* lse_part;              // [n_ranges + B - 1, Hq]
 };
 
+struct VerifyArgs {
+  const uint16_t* q;            // bf16 [total_q, Hq, 64]
+  const int32_t* qo_indptr;     // [B+1]
+  const uint16_t* k;            // bf16 [num_pages, Hkv, 16, 64]
+  const uint16_t* v;
+  const int32_t* page_indptr;   // [B+1]
+  const int32_t* page_indices;  // [nnz]
+  const int32_t* kv_len;        // [B]
+  const float* sinks;           // [Hq] or nullptr
+  int32_t batch, hq, hkv;
+  int32_t num_splits;           // S >= 1
+  int32_t chunk_pages;          // pages per split
+  float scale_log2;             // sm_scale * log2(e)
+  void* out;                    // [total_q, Hq, 64] (S == 1)
+  int32_t out_f32;
+  float* lse;                   // [total_q, Hq] or nullptr (S == 1)
+  float* o_part;                // [total_q, Hq, S, 64] (S > 1)
+  float* lse_part;              // [total_q, Hq, S]
+  int32_t write_partials;
+};
+
 struct MergeArgs {
   const float* o_parts;         // [N, H, S, 64]
   const float* lse_parts;       // [N, H, S] natural log
@@ -76,6 +97,7 @@ struct PrefillArgs {
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
 hipError_t launch_decode_balanced(const BalancedDecodeArgs& a, int group, hipStream_t stream);
 hipError_t launch_decode_finish(const BalancedDecodeArgs& a, hipStream_t stream);
+hipError_t launch_verify(const VerifyArgs& a, int group, int column_blocks, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t stream);
 

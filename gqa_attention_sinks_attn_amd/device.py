@@ -15,7 +15,8 @@ import torch
 
 from . import (BF16, F32, sink_attn_decode, sink_attn_decode_balanced,
                sink_attn_decode_balanced_workspace_size, sink_attn_decode_num_splits,
-               sink_attn_decode_workspace_size, sink_attn_prefill)
+               sink_attn_decode_workspace_size, sink_attn_prefill, sink_attn_verify,
+               sink_attn_verify_workspace_size)
 
 
 @dataclasses.dataclass
@@ -45,7 +46,8 @@ class DeviceBatch:
     lse: torch.Tensor = None
     workspace: Optional[torch.Tensor] = None
     workspace_bytes: int = 0
-    plan: str = "chunked"          # decode: "chunked" (split-KV) or "balanced"
+    plan: str = "chunked"          # decode: "chunked" (split-KV) or "balanced";
+                                   # a paged prefill batch: "verify" calls sink_attn_verify
     num_ranges: int = 0            # balanced plan: ranges per KV head, 0 = automatic
 
 
@@ -63,8 +65,10 @@ def to_device(b, device="cuda", with_lse: bool = True, out_dtype=None, plan: str
     """b: a workloads.Batch (or any object with the same attributes).
     plan / num_ranges select the decode entry point: "chunked" calls
     sink_attn_decode with the batch's num_splits, "balanced" calls
-    sink_attn_decode_balanced with num_ranges."""
-    if plan not in ("chunked", "balanced"):
+    sink_attn_decode_balanced with num_ranges.  For a paged prefill batch,
+    plan "verify" calls sink_attn_verify (with the batch's num_splits)
+    instead of sink_attn_prefill."""
+    if plan not in ("chunked", "balanced", "verify"):
         raise ValueError(plan)
     od = out_dtype if out_dtype is not None else (
         torch.float32 if getattr(b, "out_dtype", "bf16") == "f32" else torch.bfloat16)
@@ -88,6 +92,12 @@ def to_device(b, device="cuda", with_lse: bool = True, out_dtype=None, plan: str
     db.out = torch.empty((total_q, db.num_qo_heads, db.head_dim), dtype=od, device=device)
     db.lse = (torch.empty((total_q, db.num_qo_heads), dtype=torch.float32, device=device)
               if with_lse else None)
+    if db.kind == "prefill" and plan == "verify":
+        db.workspace_bytes = sink_attn_verify_workspace_size(
+            db.batch, db.num_qo_heads, db.num_kv_heads, db.head_dim, db.total_q, db.max_kv_len,
+            db.num_splits)
+        db.workspace = (torch.zeros(db.workspace_bytes, dtype=torch.uint8, device=device)
+                        if db.workspace_bytes else None)
     if db.kind == "decode" and plan == "balanced":
         db.workspace_bytes = sink_attn_decode_balanced_workspace_size(
             db.batch, db.num_qo_heads, db.num_kv_heads, db.head_dim, db.max_kv_len, db.num_ranges)
@@ -108,7 +118,13 @@ def splits_of(db: DeviceBatch) -> int:
 def run(db: DeviceBatch, stream=None) -> None:
     """Enqueue the batch's call (prefill or decode) on the current stream."""
     code = F32 if db.out_dtype == torch.float32 else BF16
-    if db.kind == "prefill":
+    if db.kind == "prefill" and db.plan == "verify":
+        sink_attn_verify(db.q, db.qo_indptr, db.k, db.v, db.kv_indptr, db.page_indices, db.kv_len,
+                         db.sinks, db.batch, db.num_qo_heads, db.num_kv_heads, db.head_dim,
+                         db.page_size, db.total_q, db.max_qlen, db.max_kv_len, db.num_splits,
+                         db.sm_scale, db.out, code, db.lse, db.workspace, db.workspace_bytes,
+                         stream)
+    elif db.kind == "prefill":
         sink_attn_prefill(db.q, db.qo_indptr, db.k, db.v, db.kv_indptr, db.page_indices,
                           db.kv_len, db.sinks, db.batch, db.num_qo_heads, db.num_kv_heads,
                           db.head_dim, db.page_size, db.total_q, db.max_qlen, db.max_kv_len,

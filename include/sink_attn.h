@@ -297,6 +297,54 @@ sink_attn_status sink_attn_decode_balanced_finish(
     void* workspace, size_t workspace_bytes,
     void* stream);
 
+/*
+ * Multi-token verification: a few new tokens per request (the drafted tokens
+ * of speculative decoding, checked in one pass) against a paged KV cache.
+ * The same operation as sink_attn_prefill on a paged cache with causal = 1,
+ * built like the split-KV decode: work parallel over heads and along the KV
+ * length, the sink in chunk 0 only (same section as sink_attn_decode), and
+ * the drafted tokens x G query heads of a request packed into the matrix
+ * columns, so a short draft streams the cache at decode speed.
+ *
+ *   q, qo_indptr     bf16 [total_q, Hq, 64]; request b owns rows
+ *                    qo_indptr[b] .. qo_indptr[b+1]-1 (its qlen_b drafted
+ *                    tokens, in order).
+ *   k_pages ... kv_len, sinks: as sink_attn_decode.  Token t of request b sits
+ *                    at position kv_len[b] - qlen_b + t (the drafted tokens
+ *                    are the last qlen_b keys of the cache) and sees keys 0 ..
+ *                    that position.  Requires 1 <= qlen_b <= kv_len[b] for
+ *                    every request with rows.
+ *   total_q, max_qlen host scalars: rows, and an upper bound of qlen_b.
+ *                    max_qlen x (Hq / Hkv) must be <= 64
+ *                    (SINK_ATTN_ERR_UNSUPPORTED otherwise: use
+ *                    sink_attn_prefill).
+ *   num_splits       as sink_attn_decode's split-KV plan (0 = automatic,
+ *                    sink_attn_decode_num_splits).
+ *   out, lse         [total_q, Hq, 64] in out_dtype; fp32 [total_q, Hq] or
+ *                    NULL (natural log).
+ *   workspace        sink_attn_verify_workspace_size() bytes (0 with one
+ *                    split): fp32 partials [total_q, Hq, S, 64], then fp32
+ *                    [total_q, Hq, S] at the next 256-byte boundary.
+ */
+size_t sink_attn_verify_workspace_size(int32_t batch, int32_t num_qo_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t total_q, int32_t max_kv_len,
+                                       int32_t num_splits);
+
+sink_attn_status sink_attn_verify(
+    const void* q, const int32_t* qo_indptr,
+    const void* k_pages, const void* v_pages,
+    const int32_t* page_indptr, const int32_t* page_indices,
+    const int32_t* kv_len,
+    const float* sinks,
+    int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t page_size,
+    int32_t total_q, int32_t max_qlen, int32_t max_kv_len, int32_t num_splits,
+    float sm_scale,
+    void* out, sink_attn_dtype out_dtype, float* lse,
+    void* workspace, size_t workspace_bytes,
+    void* stream);
+
 /* Static description of a status code. */
 const char* sink_attn_status_string(sink_attn_status s);
 

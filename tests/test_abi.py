@@ -318,3 +318,50 @@ def test_balanced_partition_covers_every_page_once(seed):
         for b, rs in reads.items():
             assert all(slots.get(s) == b for s in rs)
         assert sorted(slots) == sorted(s for rs in reads.values() for s in rs)
+
+
+# ------------------------------------------------------------- verification
+
+def call_verify(**over):
+    a = dict(q=A, qo=A, k=A, v=A, page_indptr=A, page_indices=A, kv_len=A, sinks=A, batch=64,
+             num_qo_heads=64, num_kv_heads=8, head_dim=64, page_size=16, total_q=256, max_qlen=4,
+             max_kv_len=4096, num_splits=0, sm_scale=0.125, out=A2, out_dtype=1, lse=None,
+             workspace=A3, workspace_bytes=None, stream=0)
+    a.update(over)
+    if a["workspace_bytes"] is None:
+        a["workspace_bytes"] = sa.sink_attn_verify_workspace_size(
+            a["batch"], a["num_qo_heads"], a["num_kv_heads"], 64, a["total_q"], a["max_kv_len"],
+            a["num_splits"])
+    return sa.lib().sink_attn_verify(
+        a["q"], a["qo"], a["k"], a["v"], a["page_indptr"], a["page_indices"], a["kv_len"],
+        a["sinks"], a["batch"], a["num_qo_heads"], a["num_kv_heads"], a["head_dim"],
+        a["page_size"], a["total_q"], a["max_qlen"], a["max_kv_len"], a["num_splits"],
+        a["sm_scale"], a["out"], a["out_dtype"], a["lse"], a["workspace"], a["workspace_bytes"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(qo=None), NULL), (dict(q=None), NULL), (dict(out=None), NULL), (dict(kv_len=None), NULL),
+    (dict(batch=0), SHAPE), (dict(max_qlen=300), SHAPE), (dict(total_q=-1), SHAPE),
+    (dict(max_qlen=9), UNSUP),                       # 9 x 8 = 72 rows > 64
+    (dict(num_qo_heads=64, num_kv_heads=4, max_qlen=5), UNSUP),
+    (dict(head_dim=128), UNSUP), (dict(page_size=32), UNSUP), (dict(out_dtype=4), UNSUP),
+    (dict(out=A2 + 4), MISAL), (dict(qo=A + 2), MISAL), (dict(workspace=A3 + 8), MISAL),
+    (dict(workspace=None), WS), (dict(workspace_bytes=16), WS),
+])
+def test_verify_rejects(over, code):
+    assert call_verify(**over) == code
+    assert sa.sink_attn_last_error() != ""
+
+
+def test_verify_plan_and_workspace():
+    # the split-KV planner of the decode, partials over the rows
+    S = sa.sink_attn_decode_num_splits(64, 64, 8, 4096, 0)
+    need = sa.sink_attn_verify_workspace_size(64, 64, 8, 64, 256, 4096, 0)
+    rows = 256 * 64 * S
+    assert S > 1 and need == rows * 64 * 4 + ((rows * 4 + 255) // 256) * 256
+    assert sa.sink_attn_verify_workspace_size(64, 64, 8, 64, 256, 4096, 1) == 0
+    # nothing to compute: OK without a workspace
+    assert call_verify(total_q=0, max_qlen=0, workspace=None, workspace_bytes=0) == OK
+    # G = 4: drafts of up to 16 tokens (64 rows per KV head)
+    assert call_verify(num_qo_heads=32, num_kv_heads=8, max_qlen=17) == UNSUP
