@@ -17,7 +17,8 @@ Perplexity; section "Sink attention" under "Kernels for GPT-OSS" and the
 
 Batches are duck-typed: any object with the attributes q, qo_indptr, k, v,
 kv_indptr, page_indices, kv_len, sinks, num_qo_heads, num_kv_heads,
-head_dim, page_size, sm_scale and causal (layouts in the C file's header).
+head_dim, page_size, sm_scale and causal, and optionally draft_mask (uint64
+per query row; layouts in the C file's header).
 """
 from __future__ import annotations
 
@@ -54,7 +55,7 @@ def lib():
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         ctx = [P, P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-               ctypes.c_int, ctypes.c_double, ctypes.c_int]
+               ctypes.c_int, ctypes.c_double, ctypes.c_int, P]
         L.sa_oracle_partial.argtypes = ctx + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                               P, P, ctypes.c_int]
         L.sa_oracle_attend.argtypes = ctx + [P, P, ctypes.c_int]
@@ -92,9 +93,10 @@ def _ctx(b):
     pi = arr(b.page_indices, np.int32)
     kl = arr(b.kv_len, np.int32)
     s = arr(b.sinks, np.float32)
+    dm = arr(getattr(b, "draft_mask", None), np.uint64)
     args = (_ptr(q), _ptr(qo), _ptr(k), _ptr(v), _ptr(kvi), _ptr(pi), _ptr(kl), _ptr(s),
             int(qo.shape[0] - 1), int(b.num_qo_heads), int(b.num_kv_heads), int(b.head_dim),
-            int(b.page_size), float(b.sm_scale), int(bool(b.causal)))
+            int(b.page_size), float(b.sm_scale), int(bool(b.causal)), _ptr(dm))
     return args, keep, int(qo[-1])
 
 

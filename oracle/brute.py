@@ -6,6 +6,11 @@ A second, independent formulation of the definition the C oracle computes
 head, build the full score matrix, append the head's sink as one extra
 column of logits, take a textbook softmax over each row, drop the sink
 column (it has no value vector) and multiply by V.  Meant for small shapes.
+
+With a draft mask ("Accelerating Sonar Through Speculation", Perplexity,
+section "EAGLE": tree drafts are verified under custom attention masks) the
+allowed-key matrix is built from the bits directly: prefix keys always,
+drafted key i of the request when bit i of the row's mask is set.
 """
 from __future__ import annotations
 
@@ -50,7 +55,12 @@ def brute(b, key_begin: int = 0, key_end: int | None = None, include_sink: bool 
         pos = L - n + np.arange(n)               # absolute query positions
         keys = np.arange(L)
         allowed = np.ones((n, L), dtype=bool)
-        if b.causal:
+        dmask = getattr(b, "draft_mask", None)
+        if dmask is not None:
+            bits = np.array([[(int(dmask[q0 + t]) >> i) & 1 for i in range(n)]
+                             for t in range(n)], dtype=bool)          # [n, n]
+            allowed[:, L - n:] = bits
+        elif b.causal:
             allowed &= keys[None, :] <= pos[:, None]
         allowed &= keys[None, :] >= key_begin
         if key_end is not None:

@@ -35,6 +35,14 @@
  *   kv_len keys):  causal -> j <= p;  non-causal -> every j < kv_len[b].
  *   A decode query (qlen 1) therefore sees all kv_len keys.
  *
+ *   Draft (tree) mask ("Accelerating Sonar Through Speculation", Perplexity,
+ *   section "EAGLE": tree-shaped drafts are checked with custom attention
+ *   masks).  When draft_mask is given, the qlen new tokens of a request are
+ *   its drafted tokens and the mask replaces causality among them: row t may
+ *   see every prefix key j < P = kv_len - qlen, and drafted key P + i
+ *   (i < qlen) exactly when bit i of draft_mask[row] is set.  Bits at or
+ *   above qlen are ignored.  The causal flag is not consulted.
+ *
  *   Split-KV (same section: work is parallelised along the KV length and
  *   the sink may enter only the first chunk): a partial restricts J to a
  *   key window and includes the sink only when asked; merging partials by
@@ -55,6 +63,7 @@
  *                page_size], slot j % page_size
  *   kv_len       [B] valid keys per request (NULL: contiguous indptr gap)
  *   sinks        fp32 [Hq], NULL means no sink (sigma = -inf)
+ *   draft_mask   uint64 [total_q] or NULL (no draft mask)
  *   out          double [total_q, Hq, D];  lse double [total_q, Hq]
  */
 #include <math.h>
@@ -74,6 +83,7 @@ typedef struct {
   const int32_t* page_indices;
   const int32_t* kv_len;
   const float* sinks;
+  const uint64_t* draft_mask; /* [total_q] or NULL */
   int batch, hq, hkv, d, page_size, causal;
   double sm_scale;
   int64_t key_begin, key_end; /* key window [key_begin, key_end) */
@@ -118,7 +128,7 @@ static void key_range(const ctx_t* c, int b, int64_t row, int64_t* j0, int64_t* 
   int64_t qlen = (int64_t)c->qo_indptr[b + 1] - c->qo_indptr[b];
   int64_t t = row - c->qo_indptr[b];
   int64_t hi = L;
-  if (c->causal) {
+  if (c->causal && !c->draft_mask) {
     int64_t p = L - qlen + t;  /* absolute position of the query */
     hi = p + 1 < L ? p + 1 : L;
     if (hi < 0) hi = 0;
@@ -129,6 +139,18 @@ static void key_range(const ctx_t* c, int b, int64_t row, int64_t* j0, int64_t* 
   if (hi < lo) hi = lo;
   *j0 = lo;
   *j1 = hi;
+}
+
+/* Whether key j of request b is in the allowed set of row `row` beyond its
+ * key range: only a draft mask removes keys inside [j0, j1). */
+static int key_allowed(const ctx_t* c, int b, int64_t row, int64_t j) {
+  if (!c->draft_mask) return 1;
+  int64_t L = request_kv_len(c, b);
+  int64_t qlen = (int64_t)c->qo_indptr[b + 1] - c->qo_indptr[b];
+  int64_t i = j - (L - qlen); /* index among the drafted tokens */
+  if (i < 0) return 1;        /* a prefix key */
+  if (i >= qlen || i >= 64) return 0;
+  return (int)((c->draft_mask[row] >> i) & 1u);
 }
 
 /*
@@ -151,6 +173,7 @@ static void one_row(const ctx_t* c, int64_t row, int h, double* scores,
   /* pass 1: scaled scores and the maximum over scores and sink */
   double M = sigma;
   for (int64_t j = j0; j < j1; ++j) {
+    if (!key_allowed(c, b, row, j)) { scores[j - j0] = -INFINITY; continue; }
     const uint16_t* krow = c->k + kv_row_offset(c, b, j, g);
     double dot = 0.0;
     for (int x = 0; x < D; ++x) dot += bf16_to_double(qrow[x]) * bf16_to_double(krow[x]);
@@ -174,10 +197,12 @@ static void one_row(const ctx_t* c, int64_t row, int h, double* scores,
 
   /* pass 2: the denominator, sink term included once */
   double Z = exp(sigma - M);
-  for (int64_t j = j0; j < j1; ++j) Z += exp(scores[j - j0] - M);
+  for (int64_t j = j0; j < j1; ++j)
+    if (scores[j - j0] != -INFINITY) Z += exp(scores[j - j0] - M);
 
   /* pass 3: weighted sum of values; the sink column has no value */
   for (int64_t j = j0; j < j1; ++j) {
+    if (scores[j - j0] == -INFINITY) continue; /* a masked-out key */
     double p = exp(scores[j - j0] - M) / Z;
     if (weights) weights[j - j0] = p;
     const uint16_t* vrow = c->v + kv_row_offset(c, b, j, g);
@@ -239,7 +264,7 @@ static int run_rows(const ctx_t* c, const int64_t* rows, const int32_t* heads,
       const uint16_t *v, const int32_t *kv_indptr,                            \
       const int32_t *page_indices, const int32_t *kv_len, const float *sinks, \
       int batch, int hq, int hkv, int d, int page_size, double sm_scale,      \
-      int causal
+      int causal, const uint64_t *draft_mask
 
 #define CTX_INIT(c)                                                     \
   ctx_t c;                                                              \
@@ -248,7 +273,8 @@ static int run_rows(const ctx_t* c, const int64_t* rows, const int32_t* heads,
   c.kv_indptr = kv_indptr; c.page_indices = page_indices;               \
   c.kv_len = kv_len; c.sinks = sinks; c.batch = batch; c.hq = hq;       \
   c.hkv = hkv; c.d = d; c.page_size = page_size; c.sm_scale = sm_scale; \
-  c.causal = causal; c.key_begin = 0; c.key_end = INT64_MAX;            \
+  c.causal = causal; c.draft_mask = draft_mask;                         \
+  c.key_begin = 0; c.key_end = INT64_MAX;                               \
   c.include_sink = 1
 
 /*
@@ -280,7 +306,7 @@ int sa_oracle_partial(CTX_ARGS, int64_t key_begin, int64_t key_end, int include_
 /* The full method over every (row, head). */
 int sa_oracle_attend(CTX_ARGS, double* out, double* lse, int nthreads) {
   return sa_oracle_partial(q, qo_indptr, k, v, kv_indptr, page_indices, kv_len, sinks,
-                           batch, hq, hkv, d, page_size, sm_scale, causal,
+                           batch, hq, hkv, d, page_size, sm_scale, causal, draft_mask,
                            0, INT64_MAX, 1, out, lse, nthreads);
 }
 

@@ -39,7 +39,8 @@ import numpy as np
 
 __all__ = [
     "Batch", "Mixed", "to_bf16_bits", "bf16_bits_to_f32", "make_batch",
-    "config", "CONFIG_NAMES", "K_POISON", "V_POISON",
+    "config", "CONFIG_NAMES", "K_POISON", "V_POISON", "draft_tree", "tree_mask",
+    "chain_mask",
 ]
 
 K_POISON = 8.0
@@ -82,6 +83,7 @@ class Batch:
     out_dtype: str = "f32"          # "f32" or "bf16"
     num_splits: int = 0             # decode: 0 = library's automatic plan
     name: str = ""
+    draft_mask: Optional[np.ndarray] = None  # uint64 [total_q]: drafted-token visibility
 
     @property
     def batch(self) -> int:
@@ -307,3 +309,43 @@ def mixed(seed: int = 1005, n_prefill: int = 16, n_decode: int = 256, hq: int = 
                 head_dim=d, page_size=ps, sm_scale=scale_attn, causal=True,
                 name="c5 decode part")
     return Mixed(prefill=pre, decode=dec, name=CONFIG_NAMES[5])
+
+
+# --- drafted-token trees (inputs for verification with a draft mask) ---------
+
+def draft_tree(rng, n: int, max_children: int = 4) -> np.ndarray:
+    """A random draft tree over n tokens in breadth-first order: parents[i] is
+    the index of token i's parent among the drafted tokens, or -1 when token
+    i hangs directly off the cached prefix.  Token 0 is always a root; each
+    later token picks a parent among the earlier ones that still have fewer
+    than max_children children (or becomes another root)."""
+    parents = np.full(n, -1, dtype=np.int64)
+    children = np.zeros(n, dtype=np.int64)
+    for i in range(1, n):
+        open_ = [-1] + [j for j in range(i) if children[j] < max_children]
+        p = int(open_[int(rng.integers(0, len(open_)))])
+        parents[i] = p
+        if p >= 0:
+            children[p] += 1
+    return parents
+
+
+def tree_mask(parents: Sequence[int]) -> np.ndarray:
+    """Visibility bits of a draft tree: bit j of word i is set when drafted
+    token j is token i itself or one of its ancestors.  uint64 [n], n <= 64."""
+    n = len(parents)
+    assert n <= 64
+    out = np.zeros(n, dtype=np.uint64)
+    for i in range(n):
+        w = 0
+        j = i
+        while j >= 0:
+            w |= 1 << j
+            j = int(parents[j])
+        out[i] = np.uint64(w)
+    return out
+
+
+def chain_mask(n: int) -> np.ndarray:
+    """The linear draft (each token sees itself and every earlier one)."""
+    return np.array([(1 << (i + 1)) - 1 for i in range(n)], dtype=np.uint64)
