@@ -171,8 +171,10 @@ def kv_bytes_of(b) -> int:
 def bench_extra(args, torch, sa, device, W):
     """The other workloads, each timed whole (all kernels of the call), HIP
     events: the long split decode (workload 3), both calls of the mixed batch
-    (workload 5), and a multi-token verification batch (64 requests, 4
-    drafted tokens each, KV lengths U[4, 4096], through sink_attn_prefill)."""
+    (workload 5), a multi-token verification batch (64 requests, 4 drafted
+    tokens each, KV lengths U[4, 4096]) through sink_attn_prefill and
+    sink_attn_verify, and 16-token drafts (linear, then random trees) through
+    sink_attn_verify and sink_attn_verify_tree."""
     res = {}
     steps, warm = max(5, min(args.steps, 20)), max(1, args.warmup)
 
@@ -211,15 +213,29 @@ def bench_extra(args, torch, sa, device, W):
     vb = W.make_batch(rng, kind="prefill", qlens=[4] * 64, kv_lens=L, hq=64, hkv=8, paged=True,
                       sinks="normal", name="verify: B=64 x 4 drafted tokens, L~U[4,4096], 64q/8kv, page 16")
     prefill_line("verify_4tok_prefill", vb, call="sink_attn_prefill (qlen 4 per request)")
-    db = device.to_device(vb, with_lse=False, plan="verify")
-    ms = _time_calls(torch, lambda i: device.run(db), steps, warm)
-    flops = prefill_pairs(vb) * 4 * vb.head_dim
-    res["verify_4tok"] = dict(
-        workload=vb.name, call="sink_attn_verify (automatic split plan)", ms_per_call=round(ms, 5),
-        kv_gbs=round(kv_bytes_of(vb) / (ms * 1e-3) / 1e9, 1),
-        frac_hbm=round(decode_algorithmic_bytes(vb) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        tflops=round(flops / (ms * 1e-3) / 1e12, 2))
-    del db
+
+    def verify_line(name, b, call):
+        db = device.to_device(b, with_lse=False, plan="verify")
+        ms = _time_calls(torch, lambda i: device.run(db), steps, warm)
+        # reads as a decode, plus the output rows written (fp32)
+        alg = decode_algorithmic_bytes(b) + b.total_q * b.num_qo_heads * b.head_dim * 4
+        res[name] = dict(
+            workload=b.name, call=call, ms_per_call=round(ms, 5),
+            kv_gbs=round(kv_bytes_of(b) / (ms * 1e-3) / 1e9, 1),
+            frac_hbm=round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+        del db
+        torch.cuda.empty_cache()
+
+    verify_line("verify_4tok", vb, "sink_attn_verify (automatic split plan)")
+    log("[bench] extra: tree verification batch")
+    rng = np.random.default_rng(1091)
+    L = rng.integers(16, 4096, size=64, endpoint=True)
+    tb = W.make_batch(rng, kind="prefill", qlens=[16] * 64, kv_lens=L, hq=64, hkv=8, paged=True,
+                      sinks="normal",
+                      name="tree verify: B=64 x 16-token draft trees, L~U[16,4096], 64q/8kv, page 16")
+    verify_line("verify_16tok_causal", tb, "sink_attn_verify (linear 16-token drafts, causal)")
+    tb.draft_mask = np.concatenate([W.tree_mask(W.draft_tree(rng, 16)) for _ in range(64)])
+    verify_line("verify_tree_16tok", tb, "sink_attn_verify_tree (one mask word per token)")
     return res
 
 

@@ -24,6 +24,7 @@ __all__ = [
     "sink_attn_decode_balanced", "sink_attn_decode_balanced_partial",
     "sink_attn_decode_balanced_finish", "sink_attn_decode_balanced_workspace_size",
     "sink_attn_decode_num_ranges", "sink_attn_verify", "sink_attn_verify_workspace_size",
+    "sink_attn_verify_tree", "sink_attn_verify_num_splits",
     "sink_attn_status_string", "sink_attn_last_error", "sink_attn_version",
     "SYMBOLS",
 ]
@@ -37,6 +38,7 @@ SYMBOLS = (
     "sink_attn_decode_balanced", "sink_attn_decode_balanced_partial",
     "sink_attn_decode_balanced_finish", "sink_attn_decode_balanced_workspace_size",
     "sink_attn_decode_num_ranges", "sink_attn_verify", "sink_attn_verify_workspace_size",
+    "sink_attn_verify_tree", "sink_attn_verify_num_splits",
     "sink_attn_status_string", "sink_attn_last_error", "sink_attn_version",
 )
 
@@ -95,8 +97,14 @@ def lib():
                                    _I, _I, ctypes.c_float, _P, ctypes.c_int, _P, _P,
                                    ctypes.c_size_t, _P]
     L.sink_attn_verify.restype = ctypes.c_int
-    L.sink_attn_verify_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I]
+    L.sink_attn_verify_tree.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                        _I, _I, _I, _I, ctypes.c_float, _P, ctypes.c_int, _P, _P,
+                                        ctypes.c_size_t, _P]
+    L.sink_attn_verify_tree.restype = ctypes.c_int
+    L.sink_attn_verify_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I]
     L.sink_attn_verify_workspace_size.restype = ctypes.c_size_t
+    L.sink_attn_verify_num_splits.argtypes = [_I, _I, _I, _I, _I, _I]
+    L.sink_attn_verify_num_splits.restype = _I
     L.sink_attn_status_string.argtypes = [ctypes.c_int]
     L.sink_attn_status_string.restype = ctypes.c_char_p
     L.sink_attn_last_error.argtypes = []
@@ -258,10 +266,17 @@ def sink_attn_decode_balanced_finish(page_indptr, sinks, batch, num_qo_heads, nu
 
 
 def sink_attn_verify_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim, total_q,
-                                    max_kv_len, num_splits) -> int:
+                                    max_qlen, max_kv_len, num_splits) -> int:
     return int(lib().sink_attn_verify_workspace_size(
         int(batch), int(num_qo_heads), int(num_kv_heads), int(head_dim), int(total_q),
-        int(max_kv_len), int(num_splits)))
+        int(max_qlen), int(max_kv_len), int(num_splits)))
+
+
+def sink_attn_verify_num_splits(batch, num_qo_heads, num_kv_heads, max_qlen, max_kv_len,
+                                num_splits) -> int:
+    return int(lib().sink_attn_verify_num_splits(
+        int(batch), int(num_qo_heads), int(num_kv_heads), int(max_qlen), int(max_kv_len),
+        int(num_splits)))
 
 
 def sink_attn_verify(q, qo_indptr, k_pages, v_pages, page_indptr, page_indices, kv_len, sinks,
@@ -274,3 +289,16 @@ def sink_attn_verify(q, qo_indptr, k_pages, v_pages, page_indptr, page_indices, 
         int(num_kv_heads), int(head_dim), int(page_size), int(total_q), int(max_qlen),
         int(max_kv_len), int(num_splits), float(sm_scale), _ptr(out), _dtype_code(out_dtype),
         _ptr(lse), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def sink_attn_verify_tree(q, qo_indptr, draft_mask, k_pages, v_pages, page_indptr, page_indices,
+                          kv_len, sinks, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                          total_q, max_qlen, max_kv_len, num_splits, sm_scale, out, out_dtype,
+                          lse, workspace, workspace_bytes, stream=None) -> None:
+    _check(lib().sink_attn_verify_tree(
+        _ptr(q), _ptr(qo_indptr), _ptr(draft_mask), _ptr(k_pages), _ptr(v_pages),
+        _ptr(page_indptr), _ptr(page_indices), _ptr(kv_len), _ptr(sinks), int(batch),
+        int(num_qo_heads), int(num_kv_heads), int(head_dim), int(page_size), int(total_q),
+        int(max_qlen), int(max_kv_len), int(num_splits), float(sm_scale), _ptr(out),
+        _dtype_code(out_dtype), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+        _stream(stream)))

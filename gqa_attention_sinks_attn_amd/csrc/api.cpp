@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -568,7 +569,42 @@ namespace {
 
 // Largest draft per request the verification kernel packs: qlen x G
 // (token, head) rows in at most four 16-column blocks.
-constexpr int32_t kVerifyMaxRows = 64;
+constexpr int32_t kVerifyMaxTokens = 64;   // drafted tokens per request (one mask word)
+
+// Column blocks of 16 (token, head) pairs per workgroup, 1 or 2: two blocks
+// keep the kernel at two waves per SIMD, and wider drafts run more column
+// groups, whose repeated page reads hit the XCD's L2 (measured faster than
+// four blocks at one wave per SIMD for every draft width).
+int verify_column_blocks(int32_t columns) {
+  return columns <= 16 ? 1 : 2;
+}
+
+int32_t verify_column_groups(int32_t columns) {
+  const int32_t w = 16 * verify_column_blocks(columns);
+  return (columns + w - 1) / w;
+}
+
+// Split plan of the verification kernel.  Each chunk of a request re-reads
+// its queries, merges its four waves and writes partials that a second
+// kernel merges, so splitting only pays when the grid would not fill the
+// GPU: one chunk while batch x Hkv x column groups reaches half of
+// kVerifyTargetWorkgroups (two workgroups per CU), else enough chunks to
+// reach it, each of at least 16 pages.  An explicit request is taken as
+// sink_attn_decode takes it.
+constexpr int64_t kVerifyTargetWorkgroups = 512;
+
+int32_t verify_plan_splits(int32_t batch, int32_t hkv, int32_t columns, int32_t max_kv_len,
+                           int32_t requested) {
+  if (requested > 0) return plan_splits(batch, hkv, max_kv_len, requested);
+  const int32_t pages = (max_kv_len + kPageSize - 1) / kPageSize;
+  const int64_t units = (int64_t)batch * hkv * verify_column_groups(columns);
+  if (units <= 0 || units * 2 >= kVerifyTargetWorkgroups || pages <= 16) return 1;
+  int64_t s = (kVerifyTargetWorkgroups + units - 1) / units;
+  const int64_t max_by_len = (pages + 15) / 16;
+  if (s > max_by_len) s = max_by_len;
+  if (s > 256) s = 256;
+  return s < 1 ? 1 : (int32_t)s;
+}
 
 size_t verify_workspace(int32_t total_q, int32_t num_qo_heads, int32_t head_dim, int32_t splits) {
   if (splits <= 1 || total_q <= 0) return 0;
@@ -578,25 +614,37 @@ size_t verify_workspace(int32_t total_q, int32_t num_qo_heads, int32_t head_dim,
 
 }  // namespace
 
-size_t sink_attn_verify_workspace_size(int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
-                                       int32_t head_dim, int32_t total_q, int32_t max_kv_len,
-                                       int32_t num_splits) {
-  if (batch <= 0 || num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || total_q < 0 ||
-      max_kv_len < 0 || num_splits < 0)
-    return 0;
-  return verify_workspace(total_q, num_qo_heads, head_dim,
-                          plan_splits(batch, num_kv_heads, max_kv_len, num_splits));
+int32_t sink_attn_verify_num_splits(int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                    int32_t max_qlen, int32_t max_kv_len, int32_t num_splits) {
+  if (batch <= 0 || num_qo_heads <= 0 || num_kv_heads <= 0 || num_qo_heads % num_kv_heads ||
+      max_qlen < 0 || max_kv_len < 0 || num_splits < 0)
+    return 1;
+  return verify_plan_splits(batch, num_kv_heads, max_qlen * (num_qo_heads / num_kv_heads),
+                            max_kv_len, num_splits);
 }
 
-sink_attn_status sink_attn_verify(const void* q, const int32_t* qo_indptr, const void* k_pages,
-                                  const void* v_pages, const int32_t* page_indptr,
-                                  const int32_t* page_indices, const int32_t* kv_len,
-                                  const float* sinks, int32_t batch, int32_t num_qo_heads,
-                                  int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                                  int32_t total_q, int32_t max_qlen, int32_t max_kv_len,
-                                  int32_t num_splits, float sm_scale, void* out,
-                                  sink_attn_dtype out_dtype, float* lse, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+size_t sink_attn_verify_workspace_size(int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t total_q, int32_t max_qlen,
+                                       int32_t max_kv_len, int32_t num_splits) {
+  if (batch <= 0 || num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || total_q < 0 ||
+      max_qlen < 0 || max_kv_len < 0 || num_splits < 0 || num_qo_heads % num_kv_heads)
+    return 0;
+  return verify_workspace(total_q, num_qo_heads, head_dim,
+                          sink_attn_verify_num_splits(batch, num_qo_heads, num_kv_heads, max_qlen,
+                                                      max_kv_len, num_splits));
+}
+
+namespace {
+
+sink_attn_status verify_impl(const void* q, const int32_t* qo_indptr, const void* k_pages,
+                             const void* v_pages, const int32_t* page_indptr,
+                             const int32_t* page_indices, const int32_t* kv_len,
+                             const float* sinks, const uint64_t* draft_mask, int32_t batch,
+                             int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t page_size, int32_t total_q, int32_t max_qlen,
+                             int32_t max_kv_len, int32_t num_splits, float sm_scale, void* out,
+                             sink_attn_dtype out_dtype, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   sink_attn_status st = check_decode_common(q, k_pages, v_pages, page_indptr, page_indices, kv_len,
                                             sinks, batch, num_qo_heads, num_kv_heads, head_dim,
                                             page_size, max_kv_len, num_splits, sm_scale);
@@ -606,16 +654,18 @@ sink_attn_status sink_attn_verify(const void* q, const int32_t* qo_indptr, const
   if (total_q < 0 || max_qlen < 0 || max_qlen > total_q)
     return fail(SINK_ATTN_ERR_BAD_SHAPE, "verify: total_q=%d max_qlen=%d", total_q, max_qlen);
   const int32_t G = num_qo_heads / num_kv_heads;
-  if ((int64_t)max_qlen * G > kVerifyMaxRows)
+  if (max_qlen > kVerifyMaxTokens)
     return fail(SINK_ATTN_ERR_UNSUPPORTED,
-                "verify: max_qlen x G = %d x %d rows exceeds %d (use sink_attn_prefill)", max_qlen,
-                G, kVerifyMaxRows);
+                "verify: max_qlen %d exceeds %d drafted tokens (use sink_attn_prefill)", max_qlen,
+                kVerifyMaxTokens);
+  if (draft_mask && !aligned(draft_mask, 8))
+    return fail(SINK_ATTN_ERR_MISALIGNED, "verify: draft_mask must be 8-byte aligned");
   if (out_dtype != SINK_ATTN_BF16 && out_dtype != SINK_ATTN_F32)
     return fail(SINK_ATTN_ERR_UNSUPPORTED, "verify: unknown out_dtype %d", (int)out_dtype);
   if (!aligned(out, 16) || (lse && !aligned(lse, 4)) || !aligned(qo_indptr, 4))
     return fail(SINK_ATTN_ERR_MISALIGNED,
                 "verify: out must be 16-byte, lse and qo_indptr 4-byte aligned");
-  const int32_t S = plan_splits(batch, num_kv_heads, max_kv_len, num_splits);
+  const int32_t S = verify_plan_splits(batch, num_kv_heads, max_qlen * G, max_kv_len, num_splits);
   const size_t need = verify_workspace(total_q, num_qo_heads, head_dim, S);
   if (need > 0) {
     if (!workspace)
@@ -649,13 +699,15 @@ sink_attn_status sink_attn_verify(const void* q, const int32_t* qo_indptr, const
   a.o_part = nullptr;
   a.lse_part = nullptr;
   a.write_partials = 0;
+  a.draft_mask = draft_mask;
+  const int column_blocks = verify_column_blocks(max_qlen * G);
+  a.col_groups = verify_column_groups(max_qlen * G);
   if (S > 1) {
     a.o_part = static_cast<float*>(workspace);
     a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           (size_t)total_q * num_qo_heads * S * head_dim * sizeof(float));
     a.write_partials = 1;
   }
-  const int column_blocks = (max_qlen * G + 15) / 16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = hip_status(sa::launch_verify(a, G, column_blocks, s), "verify launch");
   if (st != SINK_ATTN_OK || S == 1) return st;
@@ -669,6 +721,40 @@ sink_attn_status sink_attn_verify(const void* q, const int32_t* qo_indptr, const
   mg.out_f32 = a.out_f32;
   mg.lse = lse;
   return hip_status(sa::launch_merge(mg, s), "verify merge launch");
+}
+
+}  // namespace
+
+sink_attn_status sink_attn_verify(const void* q, const int32_t* qo_indptr, const void* k_pages,
+                                  const void* v_pages, const int32_t* page_indptr,
+                                  const int32_t* page_indices, const int32_t* kv_len,
+                                  const float* sinks, int32_t batch, int32_t num_qo_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                  int32_t total_q, int32_t max_qlen, int32_t max_kv_len,
+                                  int32_t num_splits, float sm_scale, void* out,
+                                  sink_attn_dtype out_dtype, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return verify_impl(q, qo_indptr, k_pages, v_pages, page_indptr, page_indices, kv_len, sinks,
+                     nullptr, batch, num_qo_heads, num_kv_heads, head_dim, page_size, total_q,
+                     max_qlen, max_kv_len, num_splits, sm_scale, out, out_dtype, lse, workspace,
+                     workspace_bytes, stream);
+}
+
+sink_attn_status sink_attn_verify_tree(const void* q, const int32_t* qo_indptr,
+                                       const uint64_t* draft_mask, const void* k_pages,
+                                       const void* v_pages, const int32_t* page_indptr,
+                                       const int32_t* page_indices, const int32_t* kv_len,
+                                       const float* sinks, int32_t batch, int32_t num_qo_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                       int32_t total_q, int32_t max_qlen, int32_t max_kv_len,
+                                       int32_t num_splits, float sm_scale, void* out,
+                                       sink_attn_dtype out_dtype, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (!draft_mask) return fail(SINK_ATTN_ERR_NULL_ARG, "verify_tree: draft_mask is required");
+  return verify_impl(q, qo_indptr, k_pages, v_pages, page_indptr, page_indices, kv_len, sinks,
+                     draft_mask, batch, num_qo_heads, num_kv_heads, head_dim, page_size, total_q,
+                     max_qlen, max_kv_len, num_splits, sm_scale, out, out_dtype, lse, workspace,
+                     workspace_bytes, stream);
 }
 
 }  // extern "C"

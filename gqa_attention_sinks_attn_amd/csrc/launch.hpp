@@ -65,6 +65,8 @@ struct VerifyArgs {
   float* o_part;                // [total_q, Hq, S, 64] (S > 1)
   float* lse_part;              // [total_q, Hq, S]
   int32_t write_partials;
+  const uint64_t* draft_mask;   // [total_q] drafted-token visibility, or nullptr (causal)
+  int32_t col_groups;           // Z: groups of 64 (token, head) columns per (request, KV head)
 };
 
 struct MergeArgs {

@@ -12,13 +12,22 @@
 // to score every one of them.  This kernel is the decode kernel with those
 // tokens packed into the matrix columns.
 //
-// One workgroup = (request b, KV head g, chunk c), four waves taking the
-// chunk's pages two at a time, round robin (as the split-KV decode).  The
-// rows of (b, g) are the qlen_b drafted tokens x G query heads; column
-// c' = 16 blk + (lane % 16) of column block blk is token t = c' / G, head
-// g G + c' % G.  Token t sits at position kv_len - qlen + t and sees keys
-// 0 .. kv_len - qlen + t (bottom-right causal alignment); columns past the
-// draft are padding.  Per two-page step and column block:
+// One workgroup = (request b, KV head g, chunk c, column group z), four
+// waves taking the chunk's pages two at a time, round robin (as the split-KV
+// decode).  The rows of (b, g) are the qlen_b drafted tokens x G query
+// heads; column c' = 16 (NB z + blk) + (lane % 16) is token t = c' / G, head
+// g G + c' % G; columns past the draft are padding.  Token t sits at
+// position P + t, P = kv_len - qlen, and sees keys 0 .. P + t (bottom-right
+// causal alignment), or, with a draft mask (same page, "EAGLE": tree drafts
+// are verified under custom attention masks), every prefix key plus drafted
+// key P + i when bit i of its mask word is set.  The mask is tested only on
+// the steps that reach the drafted keys.
+//
+// The Z column groups of one (request, KV head, chunk) read the same pages.
+// Workgroups are dealt to the 8 XCDs round robin, so the flat index puts
+// those Z groups on one XCD back to back, where the later reads hit its L2.
+//
+// Per two-page step and column block:
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16, K straight from registers
 //     (one load serves every column block);
 //   * the per-column causal limit masks keys; online softmax in exp2;
@@ -56,7 +65,7 @@ struct alignas(16) VerifySlot {
   float o[16 * NB][kD];
 };
 
-template <int G, int NB>
+template <int G, int NB, bool TREE>
 __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
   constexpr int kSlotBytes = (int)sizeof(VerifySlot<NB>);
   constexpr int kLdsBytes = (kWaves * kWaveLds * 2) > (kWaves * kSlotBytes)
@@ -64,8 +73,16 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kLdsBytes];
   uint16_t* lds_v = reinterpret_cast<uint16_t*>(lds_raw);
 
-  const int unit = block_x();          // b * Hkv + g
-  const int c = block_y();             // chunk
+  // flat index -> (work item = c * B * Hkv + unit, column group zg)
+  const int n_work = p.batch * p.hkv * p.num_splits;
+  const int xcd = block_x() & 7;
+  const int rest = block_x() >> 3;
+  const int zg = rest % p.col_groups;
+  const int item = (rest / p.col_groups) * 8 + xcd;
+  if (item >= n_work) return;
+  const int unit = item % (p.batch * p.hkv);   // b * Hkv + g
+  const int c = item / (p.batch * p.hkv);      // chunk
+  const int cb = 16 * NB * zg;                 // first column of the group
   const int g = unit % p.hkv;
   const int b = unit / p.hkv;
   const int lane = thread_x() & 63;
@@ -75,7 +92,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
 
   const int q0 = __builtin_amdgcn_readfirstlane(p.qo_indptr[b]);
   const int qlen = __builtin_amdgcn_readfirstlane(p.qo_indptr[b + 1]) - q0;
-  if (qlen <= 0) return;   // no rows (and q0 may be past the last row)
+  if (qlen * G <= cb) return;   // no rows in this group (q0 may be past the last row)
   const int L = __builtin_amdgcn_readfirstlane(p.kv_len[b]);
   const int n_pages = (L + kPage - 1) / kPage;
   const int pg0 = c * p.chunk_pages;
@@ -83,16 +100,24 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
   const int32_t* pages = p.page_indices + __builtin_amdgcn_readfirstlane(p.page_indptr[b]);
 
   // This lane's column in each block: token, head, key limit (keys <= lim
-  // are allowed; padding columns allow none), Q^T operand.
+  // are allowed; padding columns allow none), drafted-key bits, Q^T operand.
+  const int P = L - qlen;
   int head[NB], lim[NB];
+  uint32_t mlo[NB], mhi[NB];
   bf16x8 bq0[NB], bq1[NB];
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
-    const int cc = 16 * blk + col;
+    const int cc = cb + 16 * blk + col;
     const int t = cc / G;
     const bool live = t < qlen;
     head[blk] = g * G + cc % G;
-    lim[blk] = live ? L - qlen + t : -1;
+    lim[blk] = live ? (TREE ? P - 1 : P + t) : -1;
+    mlo[blk] = mhi[blk] = 0u;
+    if (TREE && live) {
+      const uint64_t bits = p.draft_mask[q0 + t];
+      mlo[blk] = (uint32_t)bits;
+      mhi[blk] = (uint32_t)(bits >> 32);
+    }
     const uint16_t* qh = p.q + ((int64_t)(q0 + (live ? t : 0)) * p.hq + head[blk]) * kD + 8 * grp;
     const u32x4 z = {0u, 0u, 0u, 0u};
     const u32x4 a = ld16(qh), e = ld16(qh + 32);
@@ -173,6 +198,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
 
     const int key_base = pp * kPage + 4 * grp;
     const int lim2 = two ? L : pp * kPage + kPage;   // keys of a missing second page
+    const bool draft = TREE && pp * kPage + 2 * kPage > P;   // reaches drafted keys
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
@@ -181,11 +207,27 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
       s0 = mfma16(as_bf16x8(r.k01), bq1[blk], s0);
       s1 = mfma16(as_bf16x8(r.k11), bq1[blk], s1);
       float sc[8];
+      if (draft) {
+        // drafted key P + j is visible when bit j is set (j < qlen, so the
+        // key also lies below kv_len)
+        auto seen = [&](int key) -> bool {
+          const int j = key - P;
+          const uint32_t word = j < 32 ? mlo[blk] : mhi[blk];
+          return key <= lim[blk] || ((unsigned)j < (unsigned)qlen && ((word >> (j & 31)) & 1u));
+        };
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k0 = key_base + i, k1 = key_base + kPage + i;
-        sc[i] = (k0 <= lim[blk]) ? s0[i] * p.scale_log2 : -INFINITY;
-        sc[4 + i] = (k1 <= lim[blk] && k1 < lim2) ? s1[i] * p.scale_log2 : -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          const int k0 = key_base + i, k1 = key_base + kPage + i;
+          sc[i] = seen(k0) ? s0[i] * p.scale_log2 : -INFINITY;
+          sc[4 + i] = (seen(k1) && k1 < lim2) ? s1[i] * p.scale_log2 : -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k0 = key_base + i, k1 = key_base + kPage + i;
+          sc[i] = (k0 <= lim[blk]) ? s0[i] * p.scale_log2 : -INFINITY;
+          sc[4 + i] = (k1 <= lim[blk] && k1 < lim2) ? s1[i] * p.scale_log2 : -INFINITY;
+        }
       }
       float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                        fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
@@ -245,7 +287,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
   VerifySlot<NB>& mine = slots[wave];
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
-    const int cc = 16 * blk + col;
+    const int cc = 16 * blk + col;   // column within the group
     if (grp == 0) {
       mine.m[cc] = m[blk];
       mine.d[cc] = d[blk];
@@ -261,8 +303,8 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
   const int d0 = 4 * (tt & 15);
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
-    const int cc = (tt >> 4) + 16 * k;
-    const int t = cc / G;
+    const int cc = (tt >> 4) + 16 * k;   // column within the group
+    const int t = (cb + cc) / G;
     if (t >= qlen) continue;
     float M = slots[0].m[cc];
 #pragma unroll
@@ -279,7 +321,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
     const float inv = den > 0.f ? 1.f / den : 0.f;
     acc *= inv;
     const float lse = den > 0.f ? (M + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
-    const int hh = g * G + cc % G;
+    const int hh = g * G + (cb + cc) % G;
     const int64_t row = (int64_t)(q0 + t) * p.hq + hh;
     if (!p.write_partials) {
       const int64_t base = row * kD + d0;
@@ -299,25 +341,32 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
   }
 }
 
-template <int G>
+template <int G, bool TREE>
 hipError_t launch_g(const VerifyArgs& a, int nb, hipStream_t stream) {
-  dim3 grid(a.batch * a.hkv, a.num_splits);
+  const int64_t work = (int64_t)a.batch * a.hkv * a.num_splits;
+  const int64_t blocks = (work + 7) / 8 * 8 * a.col_groups;
+  if (a.col_groups < 1 || blocks > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)blocks);
   dim3 block(256);
-  if (nb == 1) { hipLaunchKernelGGL((verify_kernel<G, 1>), grid, block, 0, stream, a); return hipGetLastError(); }
-  if (nb <= 2) { hipLaunchKernelGGL((verify_kernel<G, 2>), grid, block, 0, stream, a); return hipGetLastError(); }
-  if (nb <= 4) { hipLaunchKernelGGL((verify_kernel<G, 4>), grid, block, 0, stream, a); return hipGetLastError(); }
+  if (nb == 1) { hipLaunchKernelGGL((verify_kernel<G, 1, TREE>), grid, block, 0, stream, a); return hipGetLastError(); }
+  if (nb == 2) { hipLaunchKernelGGL((verify_kernel<G, 2, TREE>), grid, block, 0, stream, a); return hipGetLastError(); }
   return hipErrorInvalidValue;
+}
+
+template <int G>
+hipError_t launch_mode(const VerifyArgs& a, int nb, hipStream_t stream) {
+  return a.draft_mask != nullptr ? launch_g<G, true>(a, nb, stream) : launch_g<G, false>(a, nb, stream);
 }
 
 }  // namespace
 
 hipError_t launch_verify(const VerifyArgs& a, int group, int column_blocks, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_g<1>(a, column_blocks, stream);
-    case 2: return launch_g<2>(a, column_blocks, stream);
-    case 4: return launch_g<4>(a, column_blocks, stream);
-    case 8: return launch_g<8>(a, column_blocks, stream);
-    case 16: return launch_g<16>(a, column_blocks, stream);
+    case 1: return launch_mode<1>(a, column_blocks, stream);
+    case 2: return launch_mode<2>(a, column_blocks, stream);
+    case 4: return launch_mode<4>(a, column_blocks, stream);
+    case 8: return launch_mode<8>(a, column_blocks, stream);
+    case 16: return launch_mode<16>(a, column_blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }

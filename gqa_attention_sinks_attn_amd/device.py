@@ -16,7 +16,7 @@ import torch
 from . import (BF16, F32, sink_attn_decode, sink_attn_decode_balanced,
                sink_attn_decode_balanced_workspace_size, sink_attn_decode_num_splits,
                sink_attn_decode_workspace_size, sink_attn_prefill, sink_attn_verify,
-               sink_attn_verify_workspace_size)
+               sink_attn_verify_tree, sink_attn_verify_workspace_size)
 
 
 @dataclasses.dataclass
@@ -49,6 +49,7 @@ class DeviceBatch:
     plan: str = "chunked"          # decode: "chunked" (split-KV) or "balanced";
                                    # a paged prefill batch: "verify" calls sink_attn_verify
     num_ranges: int = 0            # balanced plan: ranges per KV head, 0 = automatic
+    draft_mask: Optional[torch.Tensor] = None   # verify: int64 view of the uint64 mask words
 
 
 def _bf16(a: np.ndarray, device) -> torch.Tensor:
@@ -67,7 +68,8 @@ def to_device(b, device="cuda", with_lse: bool = True, out_dtype=None, plan: str
     sink_attn_decode with the batch's num_splits, "balanced" calls
     sink_attn_decode_balanced with num_ranges.  For a paged prefill batch,
     plan "verify" calls sink_attn_verify (with the batch's num_splits)
-    instead of sink_attn_prefill."""
+    instead of sink_attn_prefill, or sink_attn_verify_tree when the batch
+    carries a draft_mask."""
     if plan not in ("chunked", "balanced", "verify"):
         raise ValueError(plan)
     od = out_dtype if out_dtype is not None else (
@@ -93,9 +95,13 @@ def to_device(b, device="cuda", with_lse: bool = True, out_dtype=None, plan: str
     db.lse = (torch.empty((total_q, db.num_qo_heads), dtype=torch.float32, device=device)
               if with_lse else None)
     if db.kind == "prefill" and plan == "verify":
+        dm = getattr(b, "draft_mask", None)
+        if dm is not None:
+            db.draft_mask = torch.from_numpy(
+                np.ascontiguousarray(dm, np.uint64).view(np.int64)).to(device)
         db.workspace_bytes = sink_attn_verify_workspace_size(
-            db.batch, db.num_qo_heads, db.num_kv_heads, db.head_dim, db.total_q, db.max_kv_len,
-            db.num_splits)
+            db.batch, db.num_qo_heads, db.num_kv_heads, db.head_dim, db.total_q, db.max_qlen,
+            db.max_kv_len, db.num_splits)
         db.workspace = (torch.zeros(db.workspace_bytes, dtype=torch.uint8, device=device)
                         if db.workspace_bytes else None)
     if db.kind == "decode" and plan == "balanced":
@@ -118,7 +124,13 @@ def splits_of(db: DeviceBatch) -> int:
 def run(db: DeviceBatch, stream=None) -> None:
     """Enqueue the batch's call (prefill or decode) on the current stream."""
     code = F32 if db.out_dtype == torch.float32 else BF16
-    if db.kind == "prefill" and db.plan == "verify":
+    if db.kind == "prefill" and db.plan == "verify" and db.draft_mask is not None:
+        sink_attn_verify_tree(db.q, db.qo_indptr, db.draft_mask, db.k, db.v, db.kv_indptr,
+                              db.page_indices, db.kv_len, db.sinks, db.batch, db.num_qo_heads,
+                              db.num_kv_heads, db.head_dim, db.page_size, db.total_q,
+                              db.max_qlen, db.max_kv_len, db.num_splits, db.sm_scale, db.out,
+                              code, db.lse, db.workspace, db.workspace_bytes, stream)
+    elif db.kind == "prefill" and db.plan == "verify":
         sink_attn_verify(db.q, db.qo_indptr, db.k, db.v, db.kv_indptr, db.page_indices, db.kv_len,
                          db.sinks, db.batch, db.num_qo_heads, db.num_kv_heads, db.head_dim,
                          db.page_size, db.total_q, db.max_qlen, db.max_kv_len, db.num_splits,

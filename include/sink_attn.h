@@ -315,11 +315,15 @@ sink_attn_status sink_attn_decode_balanced_finish(
  *                    that position.  Requires 1 <= qlen_b <= kv_len[b] for
  *                    every request with rows.
  *   total_q, max_qlen host scalars: rows, and an upper bound of qlen_b.
- *                    max_qlen x (Hq / Hkv) must be <= 64
- *                    (SINK_ATTN_ERR_UNSUPPORTED otherwise: use
- *                    sink_attn_prefill).
- *   num_splits       as sink_attn_decode's split-KV plan (0 = automatic,
- *                    sink_attn_decode_num_splits).
+ *                    max_qlen must be <= 64 (SINK_ATTN_ERR_UNSUPPORTED
+ *                    otherwise: use sink_attn_prefill).  A (request, KV
+ *                    head) has C = max_qlen x Hq / Hkv (token, head) pairs;
+ *                    each chunk runs one workgroup when C <= 16, else
+ *                    ceil(C / 32) workgroups of 32 pairs.
+ *   num_splits       0: automatic plan (sink_attn_verify_num_splits: one
+ *                    chunk per request when the grid already holds >= 256
+ *                    workgroups, else enough chunks of >= 16 pages for about
+ *                    512).  S > 0: S chunks per request, as sink_attn_decode.
  *   out, lse         [total_q, Hq, 64] in out_dtype; fp32 [total_q, Hq] or
  *                    NULL (natural log).
  *   workspace        sink_attn_verify_workspace_size() bytes (0 with one
@@ -328,11 +332,55 @@ sink_attn_status sink_attn_decode_balanced_finish(
  */
 size_t sink_attn_verify_workspace_size(int32_t batch, int32_t num_qo_heads,
                                        int32_t num_kv_heads, int32_t head_dim,
-                                       int32_t total_q, int32_t max_kv_len,
-                                       int32_t num_splits);
+                                       int32_t total_q, int32_t max_qlen,
+                                       int32_t max_kv_len, int32_t num_splits);
+
+/*
+ * The chunk count S that sink_attn_verify and sink_attn_verify_tree use for
+ * these sizes (num_splits = 0: the automatic plan above).  Host-only; 1 for
+ * invalid sizes.
+ */
+int32_t sink_attn_verify_num_splits(int32_t batch, int32_t num_qo_heads,
+                                    int32_t num_kv_heads, int32_t max_qlen,
+                                    int32_t max_kv_len, int32_t num_splits);
 
 sink_attn_status sink_attn_verify(
     const void* q, const int32_t* qo_indptr,
+    const void* k_pages, const void* v_pages,
+    const int32_t* page_indptr, const int32_t* page_indices,
+    const int32_t* kv_len,
+    const float* sinks,
+    int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t page_size,
+    int32_t total_q, int32_t max_qlen, int32_t max_kv_len, int32_t num_splits,
+    float sm_scale,
+    void* out, sink_attn_dtype out_dtype, float* lse,
+    void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/*
+ * Verification of a tree of drafted tokens ("Accelerating Sonar Through
+ * Speculation", Perplexity, section "EAGLE": tree-shaped drafts are checked in
+ * one target pass under custom attention masks; the page notes that dense
+ * full-sequence masks slowed attention by up to half).  The mask here is one
+ * 64-bit word per drafted token: the prefix is always visible, and the mask
+ * replaces causality among the drafted tokens only.
+ *
+ *   draft_mask       uint64 [total_q], 8-byte aligned, device memory.  Row r
+ *                    = qo_indptr[b] + t (drafted token t of request b) sees
+ *                    every key j < P = kv_len[b] - qlen_b, and drafted key
+ *                    P + i (i < qlen_b) exactly when bit i of draft_mask[r]
+ *                    is set.  Bits at or above qlen_b are ignored.  A token
+ *                    normally sees itself and its ancestors; a row that sees
+ *                    no key at all gets o = 0, lse = sigma.
+ *   everything else  as sink_attn_verify (same limits, same workspace size:
+ *                    sink_attn_verify_workspace_size).
+ *
+ * SINK_ATTN_ERR_NULL_ARG without a mask; SINK_ATTN_ERR_MISALIGNED if it is
+ * not 8-byte aligned.
+ */
+sink_attn_status sink_attn_verify_tree(
+    const void* q, const int32_t* qo_indptr, const uint64_t* draft_mask,
     const void* k_pages, const void* v_pages,
     const int32_t* page_indptr, const int32_t* page_indices,
     const int32_t* kv_len,

@@ -323,15 +323,17 @@ def test_balanced_partition_covers_every_page_once(seed):
 # ------------------------------------------------------------- verification
 
 def call_verify(**over):
-    a = dict(q=A, qo=A, k=A, v=A, page_indptr=A, page_indices=A, kv_len=A, sinks=A, batch=64,
+    # 8 requests: the automatic plan splits, so a missing workspace is an
+    # error and no argument set below reaches a launch
+    a = dict(q=A, qo=A, k=A, v=A, page_indptr=A, page_indices=A, kv_len=A, sinks=A, batch=8,
              num_qo_heads=64, num_kv_heads=8, head_dim=64, page_size=16, total_q=256, max_qlen=4,
              max_kv_len=4096, num_splits=0, sm_scale=0.125, out=A2, out_dtype=1, lse=None,
              workspace=A3, workspace_bytes=None, stream=0)
     a.update(over)
     if a["workspace_bytes"] is None:
         a["workspace_bytes"] = sa.sink_attn_verify_workspace_size(
-            a["batch"], a["num_qo_heads"], a["num_kv_heads"], 64, a["total_q"], a["max_kv_len"],
-            a["num_splits"])
+            a["batch"], a["num_qo_heads"], a["num_kv_heads"], 64, a["total_q"], a["max_qlen"],
+            a["max_kv_len"], a["num_splits"])
     return sa.lib().sink_attn_verify(
         a["q"], a["qo"], a["k"], a["v"], a["page_indptr"], a["page_indices"], a["kv_len"],
         a["sinks"], a["batch"], a["num_qo_heads"], a["num_kv_heads"], a["head_dim"],
@@ -343,8 +345,8 @@ def call_verify(**over):
 @pytest.mark.parametrize("over,code", [
     (dict(qo=None), NULL), (dict(q=None), NULL), (dict(out=None), NULL), (dict(kv_len=None), NULL),
     (dict(batch=0), SHAPE), (dict(max_qlen=300), SHAPE), (dict(total_q=-1), SHAPE),
-    (dict(max_qlen=9), UNSUP),                       # 9 x 8 = 72 rows > 64
-    (dict(num_qo_heads=64, num_kv_heads=4, max_qlen=5), UNSUP),
+    (dict(max_qlen=65), UNSUP),                      # more drafted tokens than a mask word
+    (dict(num_qo_heads=64, num_kv_heads=4, max_qlen=200), UNSUP),
     (dict(head_dim=128), UNSUP), (dict(page_size=32), UNSUP), (dict(out_dtype=4), UNSUP),
     (dict(out=A2 + 4), MISAL), (dict(qo=A + 2), MISAL), (dict(workspace=A3 + 8), MISAL),
     (dict(workspace=None), WS), (dict(workspace_bytes=16), WS),
@@ -355,13 +357,57 @@ def test_verify_rejects(over, code):
 
 
 def test_verify_plan_and_workspace():
-    # the split-KV planner of the decode, partials over the rows
-    S = sa.sink_attn_decode_num_splits(64, 64, 8, 4096, 0)
-    need = sa.sink_attn_verify_workspace_size(64, 64, 8, 64, 256, 4096, 0)
-    rows = 256 * 64 * S
-    assert S > 1 and need == rows * 64 * 4 + ((rows * 4 + 255) // 256) * 256
-    assert sa.sink_attn_verify_workspace_size(64, 64, 8, 64, 256, 4096, 1) == 0
+    nsp = sa.sink_attn_verify_num_splits
+    # 64 requests x 8 KV heads fill the GPU: one chunk, no workspace
+    assert nsp(64, 64, 8, 4, 4096, 0) == 1
+    assert sa.sink_attn_verify_workspace_size(64, 64, 8, 64, 256, 4, 4096, 0) == 0
+    # 8 requests: 64 (request, KV head) pairs x 1 column group -> 8 chunks
+    assert nsp(8, 64, 8, 4, 4096, 0) == 8
+    # 8-token drafts at G = 8: 64 pairs = 2 groups of 32 -> 4 chunks; at 16
+    # tokens the 4 groups already give 256 workgroups -> 1 chunk
+    assert nsp(8, 64, 8, 8, 4096, 0) == 4
+    assert nsp(8, 64, 8, 16, 4096, 0) == 1
+    # nothing to compute (no rows, no requests) plans one chunk
+    assert nsp(8, 64, 8, 0, 4096, 0) == 1 and nsp(0, 64, 8, 4, 4096, 0) == 1
+    # chunks keep >= 16 pages; short caches are not split
+    assert nsp(1, 64, 8, 2, 1024, 0) == 4 and nsp(1, 64, 8, 2, 256, 0) == 1
+    # an explicit count is taken, clamped to the page count
+    assert nsp(64, 64, 8, 4, 4096, 3) == 3 and nsp(2, 64, 8, 4, 40, 9) == 3
+    S = nsp(8, 64, 8, 4, 4096, 0)
+    need = sa.sink_attn_verify_workspace_size(8, 64, 8, 64, 32, 4, 4096, 0)
+    rows = 32 * 64 * S
+    assert need == rows * 64 * 4 + ((rows * 4 + 255) // 256) * 256
+    assert sa.sink_attn_verify_workspace_size(8, 64, 8, 64, 32, 4, 4096, 1) == 0
     # nothing to compute: OK without a workspace
     assert call_verify(total_q=0, max_qlen=0, workspace=None, workspace_bytes=0) == OK
-    # G = 4: drafts of up to 16 tokens (64 rows per KV head)
-    assert call_verify(num_qo_heads=32, num_kv_heads=8, max_qlen=17) == UNSUP
+    # up to 64 drafted tokens, whatever the group size
+    assert call_verify(num_qo_heads=32, num_kv_heads=8, max_qlen=65) == UNSUP
+    assert call_verify(num_qo_heads=16, num_kv_heads=16, max_qlen=65) == UNSUP
+
+
+def call_verify_tree(mask=A, **over):
+    a = dict(q=A, qo=A, k=A, v=A, page_indptr=A, page_indices=A, kv_len=A, sinks=A, batch=64,
+             num_qo_heads=64, num_kv_heads=8, head_dim=64, page_size=16, total_q=256, max_qlen=4,
+             max_kv_len=4096, num_splits=1, sm_scale=0.125, out=A2, out_dtype=1, lse=None,
+             workspace=None, workspace_bytes=0, stream=0)
+    a.update(over)
+    return sa.lib().sink_attn_verify_tree(
+        a["q"], a["qo"], mask, a["k"], a["v"], a["page_indptr"], a["page_indices"], a["kv_len"],
+        a["sinks"], a["batch"], a["num_qo_heads"], a["num_kv_heads"], a["head_dim"],
+        a["page_size"], a["total_q"], a["max_qlen"], a["max_kv_len"], a["num_splits"],
+        a["sm_scale"], a["out"], a["out_dtype"], a["lse"], a["workspace"], a["workspace_bytes"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(mask=None), NULL), (dict(mask=A + 4), MISAL), (dict(max_qlen=65, total_q=300), UNSUP),
+    (dict(qo=None), NULL), (dict(batch=0), SHAPE), (dict(head_dim=128), UNSUP),
+    (dict(num_splits=0, batch=8), WS),               # the automatic plan splits 8 requests
+])
+def test_verify_tree_rejects(over, code):
+    assert call_verify_tree(**over) == code
+    assert sa.sink_attn_last_error() != ""
+
+
+def test_verify_tree_empty_call_is_ok():
+    assert call_verify_tree(total_q=0, max_qlen=0) == OK

@@ -4,7 +4,13 @@ and attends causally within them and to its whole prefix -- the same
 operation as a chunked prefill at a small qlen (bottom-right alignment:
 drafted token t sits at kv_len - qlen + t).  Through both sink_attn_prefill
 and the dedicated sink_attn_verify (split-KV plans S = 0 (automatic), 1, 3,
-64), against the oracle, at the parity bar of the other GPU tests.
+64; drafts wider than 64 (token, head) pairs run several column groups),
+against the oracle, at the parity bar of the other GPU tests.
+
+Tree drafts go through sink_attn_verify_tree: random trees in breadth-first
+order, one uint64 visibility word per drafted token, against the oracle's
+draft-mask reading (prefix always visible, drafted key i visible when bit i
+is set).
 """
 from __future__ import annotations
 
@@ -40,11 +46,9 @@ def _gpu():
 
 
 @pytest.mark.parametrize("entry", ["prefill", "verify"])
-@pytest.mark.parametrize("qlen", [2, 3, 4, 6, 8])
+@pytest.mark.parametrize("qlen", [2, 3, 4, 6, 8, 16, 33])
 @pytest.mark.parametrize("hq,hkv", [(64, 8), (32, 8), (16, 16)])
 def test_verify_shapes(qlen, hq, hkv, entry):
-    if entry == "verify" and qlen * hq // hkv > 64:
-        pytest.skip("more than 64 (token, head) rows per KV head: sink_attn_prefill's shape")
     rng = np.random.default_rng(400 + qlen + hq)
     B = 24
     L = rng.integers(qlen, 3000, size=B, endpoint=True)
@@ -83,4 +87,69 @@ def test_verify_empty_requests_and_sinks():
         assert np.all(out[:, 5] == 0) and np.all(lse[:, 5] == np.inf)
         keep = [h for h in range(16) if h != 5]
         check(f"{entry} empty requests", out[:, keep], ref[:, keep], lse[:, keep], rl[:, keep],
+              bf16_out=bf16)
+
+
+def _tree_batch(seed, qlens, kv_lens, hq, hkv, sinks="normal", junk_bits=True, out_dtype="f32"):
+    rng = np.random.default_rng(seed)
+    b = W.make_batch(rng, kind="prefill", qlens=qlens, kv_lens=kv_lens, hq=hq, hkv=hkv,
+                     paged=True, sinks=sinks, out_dtype=out_dtype)
+    words = []
+    for n in qlens:
+        m = W.tree_mask(W.draft_tree(rng, int(n))) if n else np.zeros(0, np.uint64)
+        if junk_bits and n < 64:      # bits at or above qlen must be ignored
+            noise = rng.integers(0, 1 << 63, size=len(m), dtype=np.int64).astype(np.uint64)
+            m = m | (noise & np.uint64(((1 << 64) - 1) ^ ((1 << int(n)) - 1)))
+        words.append(m)
+    b.draft_mask = np.concatenate(words).astype(np.uint64)
+    return b
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+@pytest.mark.parametrize("qlen", [1, 4, 8, 16, 40, 64])
+@pytest.mark.parametrize("hq,hkv", [(64, 8), (32, 8), (16, 16)])
+def test_verify_tree_shapes(qlen, hq, hkv, splits):
+    rng = np.random.default_rng(700 + qlen + hq)
+    B = 12
+    L = rng.integers(qlen, 2500, size=B, endpoint=True)
+    L[0] = qlen                        # no prefix: the whole cache is the draft
+    L[1] = qlen + 7                    # drafted keys straddle a page boundary
+    b = _tree_batch(int(rng.integers(1 << 30)), [qlen] * B, L, hq, hkv)
+    out, lse, bf16 = run(b, "verify", splits)
+    ref, rl = oracle.attend(b)
+    check(f"tree qlen={qlen} G={hq // hkv} S={splits}", out, ref, lse, rl, bf16_out=bf16)
+
+
+def test_verify_tree_linear_draft_matches_causal_verify():
+    """A chain mask selects the causal key set: same arithmetic, same bits."""
+    rng = np.random.default_rng(760)
+    ql = rng.integers(1, 20, size=16)
+    L = ql + rng.integers(0, 3000, size=16)
+    b = W.make_batch(rng, kind="prefill", qlens=ql, kv_lens=L, hq=64, hkv=8, paged=True,
+                     sinks="normal")
+    causal_out, causal_lse, _ = run(b, "verify", 2)
+    b.draft_mask = np.concatenate([W.chain_mask(int(n)) for n in ql])
+    tree_out, tree_lse, _ = run(b, "verify", 2)
+    np.testing.assert_array_equal(tree_out, causal_out)
+    np.testing.assert_array_equal(tree_lse, causal_lse)
+
+
+def test_verify_tree_mixed_sizes_empty_rows_and_sinks():
+    """Mixed draft sizes with requests of no rows, a row that sees no key at
+    all (no prefix, empty mask word), +inf and no-sink heads, bf16 output."""
+    rng = np.random.default_rng(771)
+    ql = [5, 0, 1, 23, 0, 64, 2, 9]
+    L = [5, 30, 1, 900, 4, 2100, 2, 40]
+    s = rng.standard_normal(16).astype(np.float32)
+    s[3] = np.inf
+    s[7] = -np.inf
+    b = _tree_batch(772, ql, L, 16, 4, sinks=s, out_dtype="bf16")
+    b.draft_mask[0] = np.uint64(0)     # request 0, token 0: no prefix and no visible draft
+    for splits in (0, 1, 4):
+        out, lse, bf16 = run(b, "verify", splits)
+        ref, rl = oracle.attend(b)
+        assert np.all(out[0] == 0)
+        assert np.all(out[:, 3] == 0) and np.all(lse[:, 3] == np.inf)
+        keep = [h for h in range(16) if h != 3]
+        check(f"tree mixed S={splits}", out[:, keep], ref[:, keep], lse[:, keep], rl[:, keep],
               bf16_out=bf16)
