@@ -40,7 +40,7 @@ import numpy as np
 __all__ = [
     "Batch", "Mixed", "to_bf16_bits", "bf16_bits_to_f32", "make_batch",
     "config", "CONFIG_NAMES", "K_POISON", "V_POISON", "draft_tree", "tree_mask",
-    "chain_mask",
+    "chain_mask", "AppendBatch", "make_append_batch",
 ]
 
 K_POISON = 8.0
@@ -349,3 +349,65 @@ def tree_mask(parents: Sequence[int]) -> np.ndarray:
 def chain_mask(n: int) -> np.ndarray:
     """The linear draft (each token sees itself and every earlier one)."""
     return np.array([(1 << (i + 1)) - 1 for i in range(n)], dtype=np.uint64)
+
+
+# --- new tokens for the projection-side step (bias, rotary, paged append) ---
+
+@dataclasses.dataclass
+class AppendBatch:
+    """One step's new tokens before attention: the fused QKV projection output
+    of every new token, the projection bias, and a paged cache whose pages for
+    the new positions are already reserved (kv_len counts the new tokens)."""
+    qkv: np.ndarray                 # uint16 [T, Hq + 2 Hkv, D]
+    bias: Optional[np.ndarray]      # uint16 [(Hq + 2 Hkv) D] or None
+    qo_indptr: np.ndarray           # int32 [B+1]
+    kv_len: np.ndarray              # int32 [B], after the append
+    page_indptr: np.ndarray         # int32 [B+1]
+    page_indices: np.ndarray        # int32 [nnz]
+    k_pages: np.ndarray             # uint16 [num_pages, Hkv, page_size, D] (old contents)
+    v_pages: np.ndarray
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    name: str = ""
+
+    @property
+    def batch(self) -> int:
+        return int(self.kv_len.shape[0])
+
+    @property
+    def total_q(self) -> int:
+        return int(self.qo_indptr[-1])
+
+
+def make_append_batch(seed, *, qlens: Sequence[int], kv_lens: Sequence[int], hq: int, hkv: int,
+                      d: int = HEAD_DIM, page_size: int = PAGE_SIZE, bias: bool = True,
+                      bias_std: float = 0.5, spare_pages: int = 3, name: str = "") -> AppendBatch:
+    """Draw order: page permutation, qkv (N(0,1)), bias (N(0, bias_std)), old
+    cache contents (N(0,1)).  The pool holds the requests' pages plus
+    spare_pages unused ones, so writes outside the reserved slots show."""
+    rng = seed if isinstance(seed, np.random.Generator) else np.random.default_rng(seed)
+    qlens = np.asarray(qlens, dtype=np.int64)
+    kv_lens = np.asarray(kv_lens, dtype=np.int64)
+    assert np.all(qlens <= kv_lens)
+    B = qlens.shape[0]
+    qo = np.zeros(B + 1, np.int32)
+    qo[1:] = np.cumsum(qlens)
+    pages_per = (kv_lens + page_size - 1) // page_size
+    indptr = np.zeros(B + 1, np.int32)
+    indptr[1:] = np.cumsum(pages_per)
+    n_pages = int(indptr[-1]) + spare_pages
+    perm = rng.permutation(n_pages).astype(np.int32)
+    indices = perm[: int(indptr[-1])]
+    T = int(qo[-1])
+    H = hq + 2 * hkv
+    qkv = to_bf16_bits(rng.standard_normal((T, H, d), dtype=np.float32))
+    bb = (to_bf16_bits(bias_std * rng.standard_normal(H * d, dtype=np.float32))
+          if bias else None)
+    kp = to_bf16_bits(rng.standard_normal((max(n_pages, 1), hkv, page_size, d), dtype=np.float32))
+    vp = to_bf16_bits(rng.standard_normal((max(n_pages, 1), hkv, page_size, d), dtype=np.float32))
+    return AppendBatch(qkv=qkv, bias=bb, qo_indptr=qo, kv_len=kv_lens.astype(np.int32),
+                       page_indptr=indptr, page_indices=np.ascontiguousarray(indices),
+                       k_pages=kp, v_pages=vp, num_qo_heads=hq, num_kv_heads=hkv, head_dim=d,
+                       page_size=page_size, name=name)
