@@ -174,7 +174,8 @@ def bench_extra(args, torch, sa, device, W):
     (workload 5), a multi-token verification batch (64 requests, 4 drafted
     tokens each, KV lengths U[4, 4096]) through sink_attn_prefill and
     sink_attn_verify, and 16-token drafts (linear, then random trees) through
-    sink_attn_verify and sink_attn_verify_tree."""
+    sink_attn_verify and sink_attn_verify_tree, and the bias + rotary +
+    paged-append step on a prefill and a decode step."""
     res = {}
     steps, warm = max(5, min(args.steps, 20)), max(1, args.warmup)
 
@@ -236,7 +237,45 @@ def bench_extra(args, torch, sa, device, W):
     verify_line("verify_16tok_causal", tb, "sink_attn_verify (linear 16-token drafts, causal)")
     tb.draft_mask = np.concatenate([W.tree_mask(W.draft_tree(rng, 16)) for _ in range(64)])
     verify_line("verify_tree_16tok", tb, "sink_attn_verify_tree (one mask word per token)")
+    del tb
+    log("[bench] extra: bias + rotary + paged append")
+    append_lines(args, torch, sa, W, res, steps, warm)
     return res
+
+
+def append_lines(args, torch, sa, W, res, steps, warm):
+    """sink_attn_qkv_rope_append on a prefill step (8 x 4096 new tokens, the
+    causal-prefill shape) and a decode step (64 requests x 1 token), 64q/8kv,
+    YaRN table of 131072 positions.  Algorithmic bytes: the qkv rows read and
+    the q / k / v rows written (2 x T x (Hq + 2 Hkv) x 128 B), the table row of
+    each token (256 B), the bias and the index arrays."""
+    table = torch.empty((131072, 64), dtype=torch.float32, device="cuda")
+    sa.sink_attn_rope_table(table, 131072, 64, 150000.0, 32.0, 4096, 32.0, 1.0, 0.0)
+    for name, qlens, kvl in [
+            ("append_prefill_8x4096", [4096] * 8, [4096] * 8),
+            ("append_decode_64", [1] * 64,
+             list(np.random.default_rng(1092).integers(1, 4097, size=64)))]:
+        ab = W.make_append_batch(1093, qlens=qlens, kv_lens=kvl, hq=64, hkv=8, spare_pages=0)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()  # noqa: E731
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()  # noqa: E731
+        qkv, bias, kp, vp = dev(ab.qkv), dev(ab.bias), dev(ab.k_pages), dev(ab.v_pages)
+        qo, kl, pi, px = i32(ab.qo_indptr), i32(ab.kv_len), i32(ab.page_indptr), i32(ab.page_indices)
+        q_out = torch.empty((ab.total_q, 64, 64), dtype=torch.int16, device="cuda")
+
+        def call(i):
+            sa.sink_attn_qkv_rope_append(qkv, bias, table, 131072, qo, kl, pi, px, ab.batch, 64, 8,
+                                         64, 16, ab.total_q, 0, q_out, kp, vp)
+        ms = _time_calls(torch, call, steps, warm)
+        H = 64 + 2 * 8
+        alg = (2 * ab.total_q * H * 128 + ab.total_q * 256 + H * 128
+               + 4 * (2 * (ab.batch + 1) + ab.batch + len(ab.page_indices)))
+        res[name] = dict(workload=f"{ab.total_q} new tokens, 64q/8kv, d=64, page 16, YaRN table",
+                         call="sink_attn_qkv_rope_append", ms_per_call=round(ms, 5),
+                         achieved_gbs=round(alg / (ms * 1e-3) / 1e9, 1),
+                         frac_hbm=round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         algorithmic_bytes=int(alg))
+        del qkv, bias, kp, vp, q_out
+        torch.cuda.empty_cache()
 
 
 def bench_prefill(args, torch, sa, device, W):

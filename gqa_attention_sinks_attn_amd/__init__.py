@@ -24,7 +24,8 @@ __all__ = [
     "sink_attn_decode_balanced", "sink_attn_decode_balanced_partial",
     "sink_attn_decode_balanced_finish", "sink_attn_decode_balanced_workspace_size",
     "sink_attn_decode_num_ranges", "sink_attn_verify", "sink_attn_verify_workspace_size",
-    "sink_attn_verify_tree", "sink_attn_verify_num_splits",
+    "sink_attn_verify_tree", "sink_attn_verify_num_splits", "sink_attn_rope_table",
+    "sink_attn_qkv_rope_append",
     "sink_attn_status_string", "sink_attn_last_error", "sink_attn_version",
     "SYMBOLS",
 ]
@@ -38,7 +39,8 @@ SYMBOLS = (
     "sink_attn_decode_balanced", "sink_attn_decode_balanced_partial",
     "sink_attn_decode_balanced_finish", "sink_attn_decode_balanced_workspace_size",
     "sink_attn_decode_num_ranges", "sink_attn_verify", "sink_attn_verify_workspace_size",
-    "sink_attn_verify_tree", "sink_attn_verify_num_splits",
+    "sink_attn_verify_tree", "sink_attn_verify_num_splits", "sink_attn_rope_table",
+    "sink_attn_qkv_rope_append",
     "sink_attn_status_string", "sink_attn_last_error", "sink_attn_version",
 )
 
@@ -105,6 +107,12 @@ def lib():
     L.sink_attn_verify_workspace_size.restype = ctypes.c_size_t
     L.sink_attn_verify_num_splits.argtypes = [_I, _I, _I, _I, _I, _I]
     L.sink_attn_verify_num_splits.restype = _I
+    _D = ctypes.c_double
+    L.sink_attn_rope_table.argtypes = [_P, _I, _I, _D, _D, _I, _D, _D, _D, _P]
+    L.sink_attn_rope_table.restype = ctypes.c_int
+    L.sink_attn_qkv_rope_append.argtypes = [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                            _I, _I, _P, _P, _P, _P]
+    L.sink_attn_qkv_rope_append.restype = ctypes.c_int
     L.sink_attn_status_string.argtypes = [ctypes.c_int]
     L.sink_attn_status_string.restype = ctypes.c_char_p
     L.sink_attn_last_error.argtypes = []
@@ -302,3 +310,22 @@ def sink_attn_verify_tree(q, qo_indptr, draft_mask, k_pages, v_pages, page_indpt
         int(max_qlen), int(max_kv_len), int(num_splits), float(sm_scale), _ptr(out),
         _dtype_code(out_dtype), _ptr(lse), _ptr(workspace), int(workspace_bytes),
         _stream(stream)))
+
+
+def sink_attn_rope_table(table, max_pos, head_dim, rope_theta, factor, original_max_pos,
+                         beta_fast, beta_slow, attn_factor=0.0, stream=None) -> None:
+    _check(lib().sink_attn_rope_table(
+        _ptr(table), int(max_pos), int(head_dim), float(rope_theta), float(factor),
+        int(original_max_pos), float(beta_fast), float(beta_slow), float(attn_factor),
+        _stream(stream)))
+
+
+def sink_attn_qkv_rope_append(qkv, bias, rope_table, max_pos, qo_indptr, kv_len, page_indptr,
+                              page_indices, batch, num_qo_heads, num_kv_heads, head_dim,
+                              page_size, total_q, interleaved, q_out, k_pages, v_pages,
+                              stream=None) -> None:
+    _check(lib().sink_attn_qkv_rope_append(
+        _ptr(qkv), _ptr(bias), _ptr(rope_table), int(max_pos), _ptr(qo_indptr), _ptr(kv_len),
+        _ptr(page_indptr), _ptr(page_indices), int(batch), int(num_qo_heads),
+        int(num_kv_heads), int(head_dim), int(page_size), int(total_q), int(interleaved),
+        _ptr(q_out), _ptr(k_pages), _ptr(v_pages), _stream(stream)))

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsink_attn.so")
-SOURCES = ["api.cpp", "decode.hip", "decode_balanced.hip", "merge.hip", "prefill.hip", "verify.hip"]
+SOURCES = ["api.cpp", "decode.hip", "decode_balanced.hip", "merge.hip", "prefill.hip",
+           "rope_append.hip", "verify.hip"]
 ARCH = "gfx950"
 
 

@@ -757,4 +757,84 @@ sink_attn_status sink_attn_verify_tree(const void* q, const int32_t* qo_indptr,
                      workspace_bytes, stream);
 }
 
+sink_attn_status sink_attn_rope_table(float* table, int32_t max_pos, int32_t head_dim,
+                                      double rope_theta, double factor,
+                                      int32_t original_max_pos, double beta_fast,
+                                      double beta_slow, double attn_factor, void* stream) {
+  if (!table) return fail(SINK_ATTN_ERR_NULL_ARG, "rope_table: table is required");
+  if (max_pos < 1) return fail(SINK_ATTN_ERR_BAD_SHAPE, "rope_table: max_pos=%d", max_pos);
+  if (head_dim != kHeadDim)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "rope_table: head_dim %d (only 64)", head_dim);
+  if (!(rope_theta > 1.0) || !(factor > 0.0) || !(attn_factor >= 0.0) ||
+      !std::isfinite(rope_theta) || !std::isfinite(factor) || !std::isfinite(attn_factor))
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "rope_table: theta=%g factor=%g attn_factor=%g",
+                rope_theta, factor, attn_factor);
+  if (factor > 1.0 && (original_max_pos < 1 || !(beta_slow > 0.0) || !(beta_fast > beta_slow) ||
+                       !std::isfinite(beta_fast)))
+    return fail(SINK_ATTN_ERR_BAD_SHAPE,
+                "rope_table: YaRN needs original_max_pos >= 1 and 0 < beta_slow < beta_fast "
+                "(got %d, %g, %g)", original_max_pos, beta_slow, beta_fast);
+  if (!aligned(table, 16)) return fail(SINK_ATTN_ERR_MISALIGNED, "rope_table: table must be 16-byte aligned");
+  sa::RopeTableArgs a;
+  a.table = table;
+  a.max_pos = max_pos;
+  a.original_max_pos = original_max_pos;
+  a.base = rope_theta;
+  a.factor = factor;
+  a.beta_fast = beta_fast;
+  a.beta_slow = beta_slow;
+  a.temperature = attn_factor > 0.0 ? attn_factor : (factor > 1.0 ? 0.1 * std::log(factor) + 1.0 : 1.0);
+  return hip_status(sa::launch_rope_table(a, static_cast<hipStream_t>(stream)), "rope_table launch");
+}
+
+sink_attn_status sink_attn_qkv_rope_append(const void* qkv, const void* bias,
+                                           const float* rope_table, int32_t max_pos,
+                                           const int32_t* qo_indptr, const int32_t* kv_len,
+                                           const int32_t* page_indptr,
+                                           const int32_t* page_indices, int32_t batch,
+                                           int32_t num_qo_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t page_size, int32_t total_q,
+                                           int32_t interleaved, void* q_out, void* k_pages,
+                                           void* v_pages, void* stream) {
+  if (!qkv || !rope_table || !qo_indptr || !kv_len || !page_indptr || !page_indices || !q_out ||
+      !k_pages || !v_pages)
+    return fail(SINK_ATTN_ERR_NULL_ARG, "qkv_rope_append: only bias may be NULL");
+  if (batch < 1 || num_qo_heads < 1 || num_kv_heads < 1 || total_q < 0 || max_pos < 1)
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "qkv_rope_append: batch=%d Hq=%d Hkv=%d total_q=%d max_pos=%d",
+                batch, num_qo_heads, num_kv_heads, total_q, max_pos);
+  if (head_dim != kHeadDim || page_size != kPageSize)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "qkv_rope_append: head_dim %d, page_size %d (only 64, 16)",
+                head_dim, page_size);
+  if (interleaved != 0 && interleaved != 1)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "qkv_rope_append: interleaved must be 0 or 1");
+  if ((int64_t)total_q * 256 > 0xFFFFFFFFll || num_qo_heads + 2 * num_kv_heads > 65535 * 32)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "qkv_rope_append: grid too large");
+  if (!aligned(qkv, 16) || (bias && !aligned(bias, 16)) || !aligned(rope_table, 16) ||
+      !aligned(q_out, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
+      !aligned(qo_indptr, 4) || !aligned(kv_len, 4) || !aligned(page_indptr, 4) ||
+      !aligned(page_indices, 4))
+    return fail(SINK_ATTN_ERR_MISALIGNED,
+                "qkv_rope_append: tensors must be 16-byte, index arrays 4-byte aligned");
+  if (total_q == 0) return ok();
+  sa::RopeAppendArgs a;
+  a.qkv = static_cast<const uint16_t*>(qkv);
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.table = rope_table;
+  a.max_pos = max_pos;
+  a.qo_indptr = qo_indptr;
+  a.kv_len = kv_len;
+  a.page_indptr = page_indptr;
+  a.page_indices = page_indices;
+  a.batch = batch;
+  a.hq = num_qo_heads;
+  a.hkv = num_kv_heads;
+  a.total_q = total_q;
+  a.interleaved = interleaved;
+  a.q_out = static_cast<uint16_t*>(q_out);
+  a.k_pages = static_cast<uint16_t*>(k_pages);
+  a.v_pages = static_cast<uint16_t*>(v_pages);
+  return hip_status(sa::launch_rope_append(a, static_cast<hipStream_t>(stream)),
+                    "qkv_rope_append launch");
+}
+
 }  // extern "C"

@@ -99,7 +99,31 @@ struct PrefillArgs {
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
 hipError_t launch_decode_balanced(const BalancedDecodeArgs& a, int group, hipStream_t stream);
 hipError_t launch_decode_finish(const BalancedDecodeArgs& a, hipStream_t stream);
+struct RopeTableArgs {
+  float* table;                 // [max_pos, 64]: temperature x cos | temperature x sin
+  int32_t max_pos;
+  int32_t original_max_pos;
+  double base, factor, beta_fast, beta_slow, temperature;
+};
+
+struct RopeAppendArgs {
+  const uint16_t* qkv;          // bf16 [total_q, Hq + 2 Hkv, 64]
+  const uint16_t* bias;         // bf16 [(Hq + 2 Hkv) 64] or nullptr
+  const float* table;           // [max_pos, 64]
+  int32_t max_pos;
+  const int32_t* qo_indptr;     // [B+1]
+  const int32_t* kv_len;        // [B], the new tokens included
+  const int32_t* page_indptr;   // [B+1]
+  const int32_t* page_indices;
+  int32_t batch, hq, hkv, total_q, interleaved;
+  uint16_t* q_out;              // bf16 [total_q, Hq, 64]
+  uint16_t* k_pages;            // bf16 [num_pages, Hkv, 16, 64]
+  uint16_t* v_pages;
+};
+
 hipError_t launch_verify(const VerifyArgs& a, int group, int column_blocks, hipStream_t stream);
+hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t stream);
+hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t stream);
 

@@ -393,6 +393,76 @@ sink_attn_status sink_attn_verify_tree(
     void* workspace, size_t workspace_bytes,
     void* stream);
 
+/*
+ * The step before attention: the QKV projection's bias, YaRN rotary position
+ * encoding and the append of the new keys and values to the paged cache.
+ * "GPT-OSS on Day 0" (Perplexity), "Attention: GQA with attention sinks":
+ * YaRN positions and QKV bias are listed as model changes, with no formula;
+ * YaRN is read as published (Peng et al. 2023, "NTK-by-parts" frequencies
+ * plus the attention temperature 0.1 ln s + 1 on q and k).  "Accelerating
+ * Sonar Through Speculation" (Perplexity), "Inference with Speculative
+ * Decoding": room for the next tokens is reserved in the paged cache before
+ * the step runs.
+ *
+ * sink_attn_rope_table fills the cos/sin table once (at model load):
+ *   table            fp32 [max_pos, 64], 16-byte aligned, device memory;
+ *                    column d < 32 = T cos(p f_d), column 32 + d = T sin(p f_d)
+ *                    for position p and pair d, T the temperature.
+ *   rope_theta       base of the frequencies f_d = theta^(-2d/64) (> 1).
+ *   factor           YaRN scale s; s <= 1 gives plain rotary frequencies.
+ *   original_max_pos, beta_fast, beta_slow
+ *                    YaRN's L, beta and alpha (used when s > 1): pair d keeps
+ *                    f_d when it turns more than beta_fast times in L tokens,
+ *                    gets f_d / s when it turns fewer than beta_slow times,
+ *                    and a linear blend in the turn count between.
+ *   attn_factor      T; 0 selects 0.1 ln s + 1 (1 when s <= 1).
+ * Angles and sin/cos are evaluated in fp64.  SINK_ATTN_ERR_BAD_SHAPE for
+ * max_pos < 1, theta <= 1, factor <= 0, attn_factor < 0, or (s > 1)
+ * original_max_pos < 1 or not 0 < beta_slow < beta_fast.
+ */
+sink_attn_status sink_attn_rope_table(float* table, int32_t max_pos, int32_t head_dim,
+                                      double rope_theta, double factor,
+                                      int32_t original_max_pos, double beta_fast,
+                                      double beta_slow, double attn_factor, void* stream);
+
+/*
+ * sink_attn_qkv_rope_append: for every new token, add the bias to its fused
+ * QKV projection row, rotate the query and key heads by the token's position,
+ * write the queries to q_out and the keys and values into the token's cache
+ * slot.  Nothing else of the cache is written.
+ *
+ *   qkv              bf16 [total_q, Hq + 2 Hkv, 64]: the Hq query heads, then
+ *                    the Hkv key heads, then the Hkv value heads of each token.
+ *   bias             bf16 [(Hq + 2 Hkv) x 64] in the same head order, or NULL.
+ *                    Added before the rotation; value heads get the bias only.
+ *   rope_table, max_pos  the table above.
+ *   qo_indptr        [batch + 1]: request b's new tokens are rows
+ *                    qo_indptr[b] .. qo_indptr[b+1]-1.
+ *   kv_len           [batch]: keys of request b counting the new ones; token t
+ *                    of request b sits at position p = kv_len[b] - qlen_b + t.
+ *   page_indptr, page_indices  request b's pages (reserved for every
+ *                    position < kv_len[b]); the token's key and value go to slot
+ *                    p % 16 of page page_indices[page_indptr[b] + p / 16],
+ *                    layout [num_pages, Hkv, 16, 64] as everywhere in this
+ *                    library.
+ *   interleaved      0: dimension i pairs with i + 32 (rotate-half layout);
+ *                    1: dimension 2i pairs with 2i + 1.
+ *   q_out            bf16 [total_q, Hq, 64], ready for sink_attn_prefill,
+ *                    sink_attn_decode or sink_attn_verify.
+ * Results are rounded to bf16 (round to nearest even) once, after the fp32
+ * bias add and rotation.  A token whose position is outside [0, max_pos) or
+ * past its request's pages is skipped (nothing of it is written); device
+ * data is not otherwise checked.  Host checks as the other entry points
+ * (NULL, shapes, 16-byte alignment of tensors, 4-byte of index arrays).
+ */
+sink_attn_status sink_attn_qkv_rope_append(
+    const void* qkv, const void* bias, const float* rope_table, int32_t max_pos,
+    const int32_t* qo_indptr, const int32_t* kv_len,
+    const int32_t* page_indptr, const int32_t* page_indices,
+    int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t page_size, int32_t total_q, int32_t interleaved,
+    void* q_out, void* k_pages, void* v_pages, void* stream);
+
 /* Static description of a status code. */
 const char* sink_attn_status_string(sink_attn_status s);
 

@@ -411,3 +411,48 @@ def test_verify_tree_rejects(over, code):
 
 def test_verify_tree_empty_call_is_ok():
     assert call_verify_tree(total_q=0, max_qlen=0) == OK
+
+
+def call_rope_table(**over):
+    a = dict(table=A, max_pos=4096, head_dim=64, theta=150000.0, factor=32.0, orig=4096,
+             beta_fast=32.0, beta_slow=1.0, attn_factor=0.0, stream=0)
+    a.update(over)
+    return sa.lib().sink_attn_rope_table(a["table"], a["max_pos"], a["head_dim"], a["theta"],
+                                         a["factor"], a["orig"], a["beta_fast"], a["beta_slow"],
+                                         a["attn_factor"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(table=None), NULL), (dict(max_pos=0), SHAPE), (dict(head_dim=128), UNSUP),
+    (dict(theta=1.0), SHAPE), (dict(factor=0.0), SHAPE), (dict(attn_factor=-1.0), SHAPE),
+    (dict(orig=0), SHAPE), (dict(beta_fast=1.0), SHAPE), (dict(beta_slow=0.0), SHAPE),
+    (dict(theta=float("inf")), SHAPE), (dict(table=A + 4), MISAL),
+])
+def test_rope_table_rejects(over, code):
+    assert call_rope_table(**over) == code
+    assert sa.sink_attn_last_error() != ""
+
+
+def call_append(**over):
+    a = dict(qkv=A, bias=A, table=A, max_pos=4096, qo=A, kv_len=A, page_indptr=A,
+             page_indices=A, batch=4, hq=64, hkv=8, head_dim=64, page_size=16, total_q=0,
+             interleaved=0, q_out=A2, k=A3, v=A3, stream=0)
+    a.update(over)
+    return sa.lib().sink_attn_qkv_rope_append(
+        a["qkv"], a["bias"], a["table"], a["max_pos"], a["qo"], a["kv_len"], a["page_indptr"],
+        a["page_indices"], a["batch"], a["hq"], a["hkv"], a["head_dim"], a["page_size"],
+        a["total_q"], a["interleaved"], a["q_out"], a["k"], a["v"], a["stream"])
+
+
+# total_q = 0 everywhere: a valid set of arguments returns before any launch
+@pytest.mark.parametrize("over,code", [
+    (dict(), OK), (dict(bias=None), OK),
+    (dict(qkv=None), NULL), (dict(table=None), NULL), (dict(page_indices=None), NULL),
+    (dict(q_out=None), NULL), (dict(k=None), NULL),
+    (dict(batch=0), SHAPE), (dict(total_q=-1), SHAPE), (dict(max_pos=0), SHAPE),
+    (dict(head_dim=128), UNSUP), (dict(page_size=32), UNSUP), (dict(interleaved=2), UNSUP),
+    (dict(qkv=A + 8), MISAL), (dict(bias=A + 2), MISAL), (dict(q_out=A2 + 4), MISAL),
+    (dict(qo=A + 2), MISAL),
+])
+def test_qkv_rope_append_validation(over, code):
+    assert call_append(**over) == code
