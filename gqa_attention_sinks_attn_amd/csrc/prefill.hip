@@ -33,9 +33,10 @@
 //   * masking (causal edge, ragged tail) is applied only on tiles that
 //     straddle an edge, comparing key offsets inside the tile (constants)
 //     against one per-row limit;
-//   * the grid is flat with the query tile as its slowest index, so the
-//     longest query tiles of every (request, KV head) pair start first and
-//     the short ones fill the tail.
+//   * the grid is flat, its slowest index counting query tiles from the end
+//     of each request, so the tile that sees the most keys of every
+//     (request, KV head) pair starts first (with or without a cached
+//     prefix) and the short ones fill the tail.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -73,17 +74,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * kKBuf];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * kVBuf];
 
-  // globally longest first: the grid is flat, the q tile is the slowest index
-  const int q_tiles = (p.max_qlen + T - 1) / T;
+  // Heaviest first: the grid is flat with the round j as its slowest index,
+  // and round j takes the j-th query tile from the end of every request.  A
+  // request's last tile sees all of its keys, so round 0 holds the largest
+  // workgroup of every request (whatever its cached prefix), and work falls
+  // with j.
   const int units = p.hkv * p.batch;
   const int wg = block_x();
-  const int qt = q_tiles - 1 - wg / units;
+  const int j = wg / units;
   const int g = (wg % units) % p.hkv;
   const int b = (wg % units) / p.hkv;
   const int q_begin = p.qo_indptr[b];
   const int qlen = p.qo_indptr[b + 1] - q_begin;
+  const int qt = (qlen + T - 1) / T - 1 - j;
+  if (qt < 0) return;
   const int t0 = qt * T;
-  if (t0 >= qlen) return;
   const int kv_start = p.kv_indptr[b];
   int L;
   if (p.kv_len != nullptr) L = p.kv_len[b];
@@ -153,11 +158,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // stored (their weight is 0, and 0 x garbage must stay 0).
   const int64_t vdelta = p.v - p.k;
   auto tile_key0 = [&](int kt) { return min(kt, n_tiles - 1) * kTile; };
+  // Paged caches: the page ids of this thread's two rows are loaded one
+  // tile before the rows themselves, so a tile's K/V loads do not wait for
+  // an id load issued in the same tile.
+  int id_a = 0, id_b = 0;
+  auto load_ids = [&](int kt) {
+    if constexpr (PAGED) {
+      const int key0 = tile_key0(kt);
+      const int ka = key0 + ld_row, kb2 = key0 + 32 + ld_row;
+      id_a = p.page_indices[kv_start + ((ka < L ? ka : 0) >> 4)];
+      id_b = p.page_indices[kv_start + ((kb2 < L ? kb2 : 0) >> 4)];
+    }
+  };
+  auto row_ptr = [&](int key, int id) -> const uint16_t* {
+    if constexpr (PAGED) {
+      return p.k + (((int64_t)id * p.hkv + g) * 16 + (key & 15)) * kD;
+    } else {
+      (void)id;
+      return kv_row<PAGED>(p, p.k, g, key, kv_start);
+    }
+  };
   auto load_tile = [&](int kt) {
     const int key0 = tile_key0(kt);
     const int ka = key0 + ld_row, kb2 = key0 + 32 + ld_row;
-    const uint16_t* pa = kv_row<PAGED>(p, p.k, g, ka < L ? ka : 0, kv_start) + 8 * ld_chunk;
-    const uint16_t* pb = kv_row<PAGED>(p, p.k, g, kb2 < L ? kb2 : 0, kv_start) + 8 * ld_chunk;
+    const uint16_t* pa = row_ptr(ka < L ? ka : 0, id_a) + 8 * ld_chunk;
+    const uint16_t* pb = row_ptr(kb2 < L ? kb2 : 0, id_b) + 8 * ld_chunk;
     rk0 = ld16(pa);
     rk1 = ld16(pb);
     rv0 = ld16(pa + vdelta);
@@ -176,7 +201,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   if (n_tiles > 0) {
+    load_ids(0);
     load_tile(0);
+    load_ids(1);
     store_tile(0, 0);
   }
   __syncthreads();
@@ -190,6 +217,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int buf = kt & 1;
     load_tile(kt + 1);   // clamped: the last iteration repeats the last tile
+    load_ids(kt + 2);
     const int key0 = kt * kTile;
     const bool wave_live = !p.causal || key0 <= wave_pos_max;
     if (wave_live) {
