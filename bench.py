@@ -52,8 +52,8 @@ KV_COPIES = 4                  # rotated KV pools: 4 x 269 MB > 256 MB last-leve
 # (python bench.py --mode traffic), each scaled by the same counter on a
 # 256 MiB copy; see profiles/.  Valid for the kernel sources they were taken
 # on -- reset to None whenever decode_balanced.hip or prefill.hip changes.
-DECODE_TRAFFIC_BYTES = 260_941_603
-PREFILL_TRAFFIC_BYTES = 1_879_085_767
+DECODE_TRAFFIC_BYTES = 260_949_720
+PREFILL_TRAFFIC_BYTES = 1_887_213_294
 
 
 def log(msg: str):

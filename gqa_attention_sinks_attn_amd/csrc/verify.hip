@@ -30,7 +30,11 @@
 // Per two-page step and column block:
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16, K straight from registers
 //     (one load serves every column block);
-//   * the per-column causal limit masks keys; online softmax in exp2;
+//   * on the steps that reach the drafted keys, the per-column limit (or
+//     the draft mask) masks keys;
+//   * softmax in exp2 against a per-column reference maximum, raised (with
+//     the rescale of d and O) only when a step would push a lane's partial
+//     sum past 2^15, so most steps skip the maximum and the rescale;
 //   * O^T += V^T P^T on the same MFMA, V^T from a wave-private LDS slice
 //     read transposed with ds_read_b64_tr_b16 (read once per step, shared
 //     by the column blocks).
@@ -47,6 +51,13 @@ constexpr int kPage = 16;
 constexpr int kD = 64;
 constexpr int kVPitch = 80;                      // LDS row pitch in bf16 (160 B)
 constexpr int kWaveLds = 2 * kPage * kVPitch;    // bf16 elements per wave slice
+constexpr float kFastLimit = 32768.f;            // lane-partial step sum that forces a rescale
+
+// acc + lo(w) + hi(w) for a packed bf16 pair, accumulated in fp32
+__device__ __forceinline__ float dot2_sum(uint32_t w, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
 
 template <class T>
 __device__ __forceinline__ void settle(const T& x) {
@@ -103,26 +114,27 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
   // are allowed; padding columns allow none), drafted-key bits, Q^T operand.
   const int P = L - qlen;
   int head[NB], lim[NB];
+  bool live[NB];
   uint32_t mlo[NB], mhi[NB];
   bf16x8 bq0[NB], bq1[NB];
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
     const int cc = cb + 16 * blk + col;
     const int t = cc / G;
-    const bool live = t < qlen;
+    live[blk] = t < qlen;
     head[blk] = g * G + cc % G;
-    lim[blk] = live ? (TREE ? P - 1 : P + t) : -1;
+    lim[blk] = live[blk] ? (TREE ? P - 1 : P + t) : -1;
     mlo[blk] = mhi[blk] = 0u;
-    if (TREE && live) {
+    if (TREE && live[blk]) {
       const uint64_t bits = p.draft_mask[q0 + t];
       mlo[blk] = (uint32_t)bits;
       mhi[blk] = (uint32_t)(bits >> 32);
     }
-    const uint16_t* qh = p.q + ((int64_t)(q0 + (live ? t : 0)) * p.hq + head[blk]) * kD + 8 * grp;
+    const uint16_t* qh = p.q + ((int64_t)(q0 + (live[blk] ? t : 0)) * p.hq + head[blk]) * kD + 8 * grp;
     const u32x4 z = {0u, 0u, 0u, 0u};
     const u32x4 a = ld16(qh), e = ld16(qh + 32);
-    bq0[blk] = as_bf16x8(live ? a : z);
-    bq1[blk] = as_bf16x8(live ? e : z);
+    bq0[blk] = as_bf16x8(live[blk] ? a : z);
+    bq1[blk] = as_bf16x8(live[blk] ? e : z);
   }
 
   // Online state per column block, log2 units; the sink-carrying state
@@ -131,9 +143,11 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
   f32x4 o[NB][4];
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
-    m[blk] = -INFINITY;
+    // padding columns get a finite reference: they never force the slow
+    // path, and their sums (of exp2(0)) are never written
+    m[blk] = live[blk] ? -INFINITY : 0.f;
     d[blk] = 0.f;
-    if (c == 0 && wave == 0 && p.sinks != nullptr) {
+    if (c == 0 && wave == 0 && p.sinks != nullptr && live[blk]) {
       const float s = p.sinks[head[blk]];
       m[blk] = s * kLog2e;
       d[blk] = (grp == 0 && s != -INFINITY) ? 1.f : 0.f;
@@ -198,7 +212,10 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
 
     const int key_base = pp * kPage + 4 * grp;
     const int lim2 = two ? L : pp * kPage + kPage;   // keys of a missing second page
-    const bool draft = TREE && pp * kPage + 2 * kPage > P;   // reaches drafted keys
+    // Masks are needed only on steps that reach the drafted keys (causal or
+    // tree visibility, the end of the cache) or miss their second page.
+    const bool edge = pp * kPage + 2 * kPage > P || !two;
+    const bool draft = TREE && edge;
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
@@ -207,6 +224,11 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
       s0 = mfma16(as_bf16x8(r.k01), bq1[blk], s0);
       s1 = mfma16(as_bf16x8(r.k11), bq1[blk], s1);
       float sc[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[i] = s0[i] * p.scale_log2;
+        sc[4 + i] = s1[i] * p.scale_log2;
+      }
       if (draft) {
         // drafted key P + j is visible when bit j is set (j < qlen, so the
         // key also lies below kv_len)
@@ -218,37 +240,47 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int k0 = key_base + i, k1 = key_base + kPage + i;
-          sc[i] = seen(k0) ? s0[i] * p.scale_log2 : -INFINITY;
-          sc[4 + i] = (seen(k1) && k1 < lim2) ? s1[i] * p.scale_log2 : -INFINITY;
+          if (!seen(k0)) sc[i] = -INFINITY;
+          if (!(seen(k1) && k1 < lim2)) sc[4 + i] = -INFINITY;
         }
-      } else {
+      } else if (edge) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int k0 = key_base + i, k1 = key_base + kPage + i;
-          sc[i] = (k0 <= lim[blk]) ? s0[i] * p.scale_log2 : -INFINITY;
-          sc[4 + i] = (k1 <= lim[blk] && k1 < lim2) ? s1[i] * p.scale_log2 : -INFINITY;
+          if (!(k0 <= lim[blk])) sc[i] = -INFINITY;
+          if (!(k1 <= lim[blk] && k1 < lim2)) sc[4 + i] = -INFINITY;
         }
       }
-      float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-      mx = fmaxf(mx, xor_lane(mx, 16));
-      mx = fmaxf(mx, xor_lane(mx, 32));
-      const float m_new = fmaxf(m[blk], mx);
-      const float alpha = (m[blk] == m_new) ? 1.f : fast_exp2(m[blk] - m_new);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      float pr[8];
+      // Exponentiate against the column's reference maximum m.  The fast
+      // path holds while every lane's partial sum stays below kFastLimit
+      // and the column has a reference; otherwise take the true maximum of
+      // the step, rescale d and O, and exponentiate again.  Either way the
+      // result is the online softmax's.
+      uint32_t pw[4];
       float psum = 0.f;
+      auto expo = [&](float m_use) {
+        psum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pr[i] = fast_exp2(sc[i] - m_use);
-        psum += pr[i];
+        for (int i = 0; i < 4; ++i) {
+          pw[i] = pack_bf16x2(fast_exp2(sc[2 * i] - m_use), fast_exp2(sc[2 * i + 1] - m_use));
+          psum = dot2_sum(pw[i], psum);
+        }
+      };
+      expo(m[blk]);
+      float alpha = 1.f;
+      if (__any(!(psum <= kFastLimit) || m[blk] == -INFINITY)) {
+        float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                         fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        mx = fmaxf(mx, xor_lane(mx, 16));
+        mx = fmaxf(mx, xor_lane(mx, 32));
+        const float m_new = fmaxf(m[blk], mx);
+        alpha = (m[blk] == m_new) ? 1.f : fast_exp2(m[blk] - m_new);
+        m[blk] = m_new;
+        expo(m_new == -INFINITY ? 0.f : m_new);
       }
       d[blk] = d[blk] * alpha + psum;
-      m[blk] = m_new;
       // P^T operand: slot j <-> key (j < 4 ? 4 grp + j : 16 + 4 grp + j - 4)
-      const u32x4 pw = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                        pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
-      const bf16x8 pb = as_bf16x8(pw);
+      const bf16x8 pb = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[blk][db] = mfma16(vt[db], pb, o[blk][db] * alpha);
     }
@@ -262,16 +294,23 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
       ids = pages[min(pp + (lane & 1), pg1 - 1)];
       settle(ids);
     }
-    StepRegs ra, rb;
+    // three register sets: the loads of step i + 2 are in flight while
+    // step i is processed
+    StepRegs ra, rb, rc;
     issue(ra, pids(0));
-    for (int i = 0; i < nb; i += 2) {
-      issue(rb, pids(min(i + 1, nb - 1)));
+    issue(rb, pids(min(1, nb - 1)));
+    for (int i = 0; i < nb; i += 3) {
+      issue(rc, pids(min(i + 2, nb - 1)));
       __builtin_amdgcn_sched_barrier(0);
       process(ra, blk0 + i);
       __builtin_amdgcn_sched_barrier(0);
-      issue(ra, pids(min(i + 2, nb - 1)));
+      issue(ra, pids(min(i + 3, nb - 1)));
       __builtin_amdgcn_sched_barrier(0);
       if (i + 1 < nb) process(rb, blk0 + i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(rb, pids(min(i + 4, nb - 1)));
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 2 < nb) process(rc, blk0 + i + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
