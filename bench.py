@@ -238,6 +238,14 @@ def bench_extra(args, torch, sa, device, W):
     tb.draft_mask = np.concatenate([W.tree_mask(W.draft_tree(rng, 16)) for _ in range(64)])
     verify_line("verify_tree_16tok", tb, "sink_attn_verify_tree (one mask word per token)")
     del tb
+    rng = np.random.default_rng(1094)
+    L = rng.integers(32, 4096, size=64, endpoint=True)
+    wb = W.make_batch(rng, kind="prefill", qlens=[32] * 64, kv_lens=L, hq=64, hkv=8, paged=True,
+                      sinks="normal",
+                      name="tree verify: B=64 x 32-token draft trees, L~U[32,4096], 64q/8kv, page 16")
+    wb.draft_mask = np.concatenate([W.tree_mask(W.draft_tree(rng, 32)) for _ in range(64)])
+    verify_line("verify_tree_32tok", wb, "sink_attn_verify_tree (automatic plan: prefill tiles)")
+    del wb
     log("[bench] extra: bias + rotary + paged append")
     append_lines(args, torch, sa, W, res, steps, warm)
     return res

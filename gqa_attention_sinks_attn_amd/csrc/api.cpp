@@ -256,6 +256,7 @@ sink_attn_status sink_attn_prefill(const void* q, const int32_t* qo_indptr, cons
   a.out = out;
   a.out_f32 = out_dtype == SINK_ATTN_F32;
   a.lse = lse;
+  a.draft_mask = nullptr;
   return hip_status(sa::launch_prefill(a, num_qo_heads / num_kv_heads,
                                        static_cast<hipStream_t>(stream)),
                     "prefill launch");
@@ -593,9 +594,19 @@ int32_t verify_column_groups(int32_t columns) {
 // sink_attn_decode takes it.
 constexpr int64_t kVerifyTargetWorkgroups = 512;
 
+// Wide drafts under the automatic plan run the prefill kernel instead: its
+// 256-row tiles on 32x32 MFMAs, K/V staged in LDS once per workgroup, beat
+// column groups on 16x16 MFMAs past 128 (token, head) pairs per KV head
+// (measured: 4 groups at 16 tokens x G = 8 tie, 8 groups at 32 tokens lose
+// ~1.8x).  Group sizes the prefill kernel is built for only.
+bool verify_uses_prefill(int32_t group, int32_t columns, int32_t requested) {
+  return requested == 0 && columns > 128 && (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
 int32_t verify_plan_splits(int32_t batch, int32_t hkv, int32_t columns, int32_t max_kv_len,
-                           int32_t requested) {
+                           int32_t requested, int32_t group) {
   if (requested > 0) return plan_splits(batch, hkv, max_kv_len, requested);
+  if (verify_uses_prefill(group, columns, requested)) return 1;
   const int32_t pages = (max_kv_len + kPageSize - 1) / kPageSize;
   const int64_t units = (int64_t)batch * hkv * verify_column_groups(columns);
   if (units <= 0 || units * 2 >= kVerifyTargetWorkgroups || pages <= 16) return 1;
@@ -619,8 +630,8 @@ int32_t sink_attn_verify_num_splits(int32_t batch, int32_t num_qo_heads, int32_t
   if (batch <= 0 || num_qo_heads <= 0 || num_kv_heads <= 0 || num_qo_heads % num_kv_heads ||
       max_qlen < 0 || max_kv_len < 0 || num_splits < 0)
     return 1;
-  return verify_plan_splits(batch, num_kv_heads, max_qlen * (num_qo_heads / num_kv_heads),
-                            max_kv_len, num_splits);
+  const int32_t G = num_qo_heads / num_kv_heads;
+  return verify_plan_splits(batch, num_kv_heads, max_qlen * G, max_kv_len, num_splits, G);
 }
 
 size_t sink_attn_verify_workspace_size(int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
@@ -665,7 +676,7 @@ sink_attn_status verify_impl(const void* q, const int32_t* qo_indptr, const void
   if (!aligned(out, 16) || (lse && !aligned(lse, 4)) || !aligned(qo_indptr, 4))
     return fail(SINK_ATTN_ERR_MISALIGNED,
                 "verify: out must be 16-byte, lse and qo_indptr 4-byte aligned");
-  const int32_t S = verify_plan_splits(batch, num_kv_heads, max_qlen * G, max_kv_len, num_splits);
+  const int32_t S = verify_plan_splits(batch, num_kv_heads, max_qlen * G, max_kv_len, num_splits, G);
   const size_t need = verify_workspace(total_q, num_qo_heads, head_dim, S);
   if (need > 0) {
     if (!workspace)
@@ -677,6 +688,30 @@ sink_attn_status verify_impl(const void* q, const int32_t* qo_indptr, const void
       return fail(SINK_ATTN_ERR_MISALIGNED, "verify: workspace must be 16-byte aligned");
   }
   if (total_q == 0 || max_qlen == 0) return ok();
+
+  if (verify_uses_prefill(G, max_qlen * G, num_splits)) {
+    sa::PrefillArgs pa;
+    pa.q = static_cast<const uint16_t*>(q);
+    pa.qo_indptr = qo_indptr;
+    pa.k = static_cast<const uint16_t*>(k_pages);
+    pa.v = static_cast<const uint16_t*>(v_pages);
+    pa.kv_indptr = page_indptr;
+    pa.page_indices = page_indices;
+    pa.kv_len = kv_len;
+    pa.sinks = sinks;
+    pa.batch = batch;
+    pa.hq = num_qo_heads;
+    pa.hkv = num_kv_heads;
+    pa.max_qlen = max_qlen;
+    pa.causal = 1;
+    pa.scale_log2 = sm_scale * 1.4426950408889634f;
+    pa.out = out;
+    pa.out_f32 = out_dtype == SINK_ATTN_F32;
+    pa.lse = lse;
+    pa.draft_mask = draft_mask;
+    return hip_status(sa::launch_prefill(pa, G, static_cast<hipStream_t>(stream)),
+                      "verify (prefill tiles) launch");
+  }
 
   sa::VerifyArgs a;
   a.q = static_cast<const uint16_t*>(q);

@@ -319,7 +319,10 @@ sink_attn_status sink_attn_decode_balanced_finish(
  *                    otherwise: use sink_attn_prefill).  A (request, KV
  *                    head) has C = max_qlen x Hq / Hkv (token, head) pairs;
  *                    each chunk runs one workgroup when C <= 16, else
- *                    ceil(C / 32) workgroups of 32 pairs.
+ *                    ceil(C / 32) workgroups of 32 pairs.  Under the
+ *                    automatic plan, C > 128 with Hq / Hkv in {1, 2, 4, 8}
+ *                    runs the prefill kernel's 256-row tiles instead (one
+ *                    chunk, no workspace).
  *   num_splits       0: automatic plan (sink_attn_verify_num_splits: one
  *                    chunk per request when the grid already holds >= 256
  *                    workgroups, else enough chunks of >= 16 pages for about

@@ -367,6 +367,11 @@ def test_verify_plan_and_workspace():
     # tokens the 4 groups already give 256 workgroups -> 1 chunk
     assert nsp(8, 64, 8, 8, 4096, 0) == 4
     assert nsp(8, 64, 8, 16, 4096, 0) == 1
+    # past 128 pairs per KV head the automatic plan runs prefill tiles: no split
+    assert nsp(2, 64, 8, 32, 4096, 0) == 1
+    assert sa.sink_attn_verify_workspace_size(2, 64, 8, 64, 64, 32, 4096, 0) == 0
+    # ... for the group sizes the prefill kernel has (G = 16 keeps column groups)
+    assert nsp(2, 64, 4, 32, 4096, 0) == 4
     # nothing to compute (no rows, no requests) plans one chunk
     assert nsp(8, 64, 8, 0, 4096, 0) == 1 and nsp(0, 64, 8, 4, 4096, 0) == 1
     # chunks keep >= 16 pages; short caches are not split
