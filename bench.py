@@ -174,8 +174,9 @@ def bench_extra(args, torch, sa, device, W):
     (workload 5), a multi-token verification batch (64 requests, 4 drafted
     tokens each, KV lengths U[4, 4096]) through sink_attn_prefill and
     sink_attn_verify, and 16-token drafts (linear, then random trees) through
-    sink_attn_verify and sink_attn_verify_tree, and the bias + rotary +
-    paged-append step on a prefill and a decode step."""
+    sink_attn_verify and sink_attn_verify_tree, the bias + rotary +
+    paged-append step on a prefill and a decode step, and a whole decode
+    step (append + attend) eager and replayed from a captured graph."""
     res = {}
     steps, warm = max(5, min(args.steps, 20)), max(1, args.warmup)
 
@@ -248,7 +249,57 @@ def bench_extra(args, torch, sa, device, W):
     del wb
     log("[bench] extra: bias + rotary + paged append")
     append_lines(args, torch, sa, W, res, steps, warm)
+    log("[bench] extra: decode step, eager and as a captured graph")
+    graph_step_line(torch, sa, W, res, steps, warm)
     return res
+
+
+def graph_step_line(torch, sa, W, res, steps, warm):
+    """One decode step of 64 requests (64q/8kv, KV lengths U[1, 4096]): the
+    new token's bias + rotary + paged append, then the automatic-plan decode
+    (balanced first pass + finish), launched eagerly and replayed from one
+    captured HIP graph.  Whole step per call, HIP events."""
+    B, Hq, Hkv = 64, 64, 8
+    rng = np.random.default_rng(1095)
+    L = rng.integers(1, 4097, size=B)
+    ab = W.make_append_batch(rng, qlens=[1] * B, kv_lens=L, hq=Hq, hkv=Hkv, spare_pages=0)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()  # noqa: E731
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()  # noqa: E731
+    qkv, bias, kp, vp = dev(ab.qkv), dev(ab.bias), dev(ab.k_pages), dev(ab.v_pages)
+    qo, kl, pi, px = i32(ab.qo_indptr), i32(ab.kv_len), i32(ab.page_indptr), i32(ab.page_indices)
+    table = torch.empty((4096, 64), dtype=torch.float32, device="cuda")
+    sa.sink_attn_rope_table(table, 4096, 64, 150000.0, 32.0, 4096, 32.0, 1.0, 0.0)
+    sinks = torch.from_numpy(rng.standard_normal(Hq).astype(np.float32)).cuda()
+    q = torch.empty((B, Hq, 64), dtype=torch.int16, device="cuda")
+    out = torch.empty((B, Hq, 64), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    max_L = int(L.max())
+    ws_bytes = sa.sink_attn_decode_workspace_size(B, Hq, Hkv, 64, max_L, 0)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+
+    def call(i=0):
+        sa.sink_attn_qkv_rope_append(qkv, bias, table, 4096, qo, kl, pi, px, B, Hq, Hkv, 64, 16,
+                                     B, 0, q, kp, vp)
+        sa.sink_attn_decode(q, kp, vp, pi, px, kl, sinks, B, Hq, Hkv, 64, 16, max_L, 0, 0.125, out,
+                            sa.F32, lse, ws, ws_bytes)
+
+    eager = _time_calls(torch, call, steps, warm)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        call()
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        call()
+    torch.cuda.synchronize()
+    replay = _time_calls(torch, lambda i: graph.replay(), steps, warm)
+    kv = int(L.sum()) * 2 * Hkv * 64 * 2
+    res["decode_step_graph"] = dict(
+        workload=f"decode step: B={B}, L~U[1,4096], 64q/8kv; append + attend",
+        call="sink_attn_qkv_rope_append + sink_attn_decode (balanced), 3 kernels",
+        ms_eager=round(eager, 5), ms_graph_replay=round(replay, 5),
+        kv_gbs_graph=round(kv / (replay * 1e-3) / 1e9, 1))
+    del graph
 
 
 def append_lines(args, torch, sa, W, res, steps, warm):
