@@ -153,3 +153,23 @@ def test_verify_tree_mixed_sizes_empty_rows_and_sinks():
         keep = [h for h in range(16) if h != 3]
         check(f"tree mixed S={splits}", out[:, keep], ref[:, keep], lse[:, keep], rl[:, keep],
               bf16_out=bf16)
+
+
+@pytest.mark.parametrize("tree", [False, True])
+def test_verify_long_context_split_plan(tree):
+    """Two requests at the maximum context of the long-decode workload
+    (131,072 keys): the automatic plan splits each request into many chunks
+    (sink in chunk 0 only) and merges them; drafted keys sit at the very end
+    of the cache."""
+    rng = np.random.default_rng(790 + int(tree))
+    ql = [4, 2]
+    b = W.make_batch(rng, kind="prefill", qlens=ql, kv_lens=[131072, 131072 - 5], hq=64, hkv=8,
+                     paged=True, sinks="normal")
+    if tree:
+        b.draft_mask = np.concatenate([W.tree_mask(W.draft_tree(rng, n)) for n in ql])
+    from gqa_attention_sinks_attn_amd import sink_attn_verify_num_splits
+    S = sink_attn_verify_num_splits(2, 64, 8, 4, 131072, 0)
+    assert S > 1
+    out, lse, bf16 = run(b, "verify", 0)
+    ref, rl = oracle.attend(b)
+    check(f"long context tree={tree} S={S}", out, ref, lse, rl, bf16_out=bf16)
