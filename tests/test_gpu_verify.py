@@ -173,3 +173,24 @@ def test_verify_long_context_split_plan(tree):
     out, lse, bf16 = run(b, "verify", 0)
     ref, rl = oracle.attend(b)
     check(f"long context tree={tree} S={S}", out, ref, lse, rl, bf16_out=bf16)
+
+
+@pytest.mark.parametrize("qlen,tree", [(4, False), (4, True), (40, True), (33, False)])
+def test_verify_without_lse_bf16(qlen, tree):
+    """lse = NULL and bf16 output, on the column-group kernel (4 tokens) and
+    on the prefill tiles the automatic plan picks for wide drafts (33, 40)."""
+    from gqa_attention_sinks_attn_amd import device
+    rng = np.random.default_rng(810 + qlen + int(tree))
+    B = 10
+    L = rng.integers(qlen, 2000, size=B, endpoint=True)
+    b = W.make_batch(rng, kind="prefill", qlens=[qlen] * B, kv_lens=L, hq=64, hkv=8, paged=True,
+                     sinks="normal", out_dtype="bf16")
+    if tree:
+        b.draft_mask = np.concatenate([W.tree_mask(W.draft_tree(rng, qlen)) for _ in range(B)])
+    db = device.to_device(b, with_lse=False, plan="verify")
+    assert db.lse is None
+    device.run(db)
+    torch.cuda.synchronize()
+    out = db.out.float().cpu().numpy().astype(np.float64)
+    ref, _ = oracle.attend(b)
+    check(f"no lse qlen={qlen} tree={tree}", out, ref, bf16_out=True)
