@@ -217,10 +217,7 @@ def bench_extra(args, torch, sa, device, W):
     decode_line("c5_decode", mx.decode)
     del mx
     log("[bench] extra: verification batch")
-    rng = np.random.default_rng(1090)
-    L = rng.integers(4, 4096, size=64, endpoint=True)
-    vb = W.make_batch(rng, kind="prefill", qlens=[4] * 64, kv_lens=L, hq=64, hkv=8, paged=True,
-                      sinks="normal", name="verify: B=64 x 4 drafted tokens, L~U[4,4096], 64q/8kv, page 16")
+    vb = W.verify_workload("verify_4tok")
     prefill_line("verify_4tok_prefill", vb, call="sink_attn_prefill (qlen 4 per request)")
 
     def verify_line(name, b, call):
@@ -237,23 +234,12 @@ def bench_extra(args, torch, sa, device, W):
 
     verify_line("verify_4tok", vb, "sink_attn_verify (automatic split plan)")
     log("[bench] extra: tree verification batch")
-    rng = np.random.default_rng(1091)
-    L = rng.integers(16, 4096, size=64, endpoint=True)
-    tb = W.make_batch(rng, kind="prefill", qlens=[16] * 64, kv_lens=L, hq=64, hkv=8, paged=True,
-                      sinks="normal",
-                      name="tree verify: B=64 x 16-token draft trees, L~U[16,4096], 64q/8kv, page 16")
-    verify_line("verify_16tok_causal", tb, "sink_attn_verify (linear 16-token drafts, causal)")
-    tb.draft_mask = np.concatenate([W.tree_mask(W.draft_tree(rng, 16)) for _ in range(64)])
-    verify_line("verify_tree_16tok", tb, "sink_attn_verify_tree (one mask word per token)")
-    del tb
-    rng = np.random.default_rng(1094)
-    L = rng.integers(32, 4096, size=64, endpoint=True)
-    wb = W.make_batch(rng, kind="prefill", qlens=[32] * 64, kv_lens=L, hq=64, hkv=8, paged=True,
-                      sinks="normal",
-                      name="tree verify: B=64 x 32-token draft trees, L~U[32,4096], 64q/8kv, page 16")
-    wb.draft_mask = np.concatenate([W.tree_mask(W.draft_tree(rng, 32)) for _ in range(64)])
-    verify_line("verify_tree_32tok", wb, "sink_attn_verify_tree (automatic plan: prefill tiles)")
-    del wb
+    verify_line("verify_16tok_causal", W.verify_workload("verify_16tok"),
+                "sink_attn_verify (linear 16-token drafts, causal)")
+    verify_line("verify_tree_16tok", W.verify_workload("verify_tree_16tok"),
+                "sink_attn_verify_tree (one mask word per token)")
+    verify_line("verify_tree_32tok", W.verify_workload("verify_tree_32tok"),
+                "sink_attn_verify_tree (automatic plan: prefill tiles)")
     log("[bench] extra: bias + rotary + paged append")
     append_lines(args, torch, sa, W, res, steps, warm)
     log("[bench] extra: decode step, eager and as a captured graph")
@@ -317,11 +303,8 @@ def append_lines(args, torch, sa, W, res, steps, warm):
     each token (256 B), the bias and the index arrays."""
     table = torch.empty((131072, 64), dtype=torch.float32, device="cuda")
     sa.sink_attn_rope_table(table, 131072, 64, 150000.0, 32.0, 4096, 32.0, 1.0, 0.0)
-    for name, qlens, kvl in [
-            ("append_prefill_8x4096", [4096] * 8, [4096] * 8),
-            ("append_decode_64", [1] * 64,
-             list(np.random.default_rng(1092).integers(1, 4097, size=64)))]:
-        ab = W.make_append_batch(1093, qlens=qlens, kv_lens=kvl, hq=64, hkv=8, spare_pages=0)
+    for name in W.APPEND_WORKLOADS:
+        ab = W.append_workload(name)
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()  # noqa: E731
         i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()  # noqa: E731
         qkv, bias, kp, vp = dev(ab.qkv), dev(ab.bias), dev(ab.k_pages), dev(ab.v_pages)

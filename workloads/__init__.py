@@ -40,7 +40,8 @@ import numpy as np
 __all__ = [
     "Batch", "Mixed", "to_bf16_bits", "bf16_bits_to_f32", "make_batch",
     "config", "CONFIG_NAMES", "K_POISON", "V_POISON", "draft_tree", "tree_mask",
-    "chain_mask", "AppendBatch", "make_append_batch",
+    "chain_mask", "AppendBatch", "make_append_batch", "verify_workload", "append_workload",
+    "VERIFY_WORKLOADS", "APPEND_WORKLOADS",
 ]
 
 K_POISON = 8.0
@@ -411,3 +412,41 @@ def make_append_batch(seed, *, qlens: Sequence[int], kv_lens: Sequence[int], hq:
                        page_indptr=indptr, page_indices=np.ascontiguousarray(indices),
                        k_pages=kp, v_pages=vp, num_qo_heads=hq, num_kv_heads=hkv, head_dim=d,
                        page_size=page_size, name=name)
+
+
+# --- the verification and append batches the benchmark times ----------------
+
+VERIFY_WORKLOADS = ("verify_4tok", "verify_16tok", "verify_tree_16tok", "verify_tree_32tok")
+APPEND_WORKLOADS = ("append_prefill_8x4096", "append_decode_64")
+
+
+def verify_workload(name: str) -> Batch:
+    """64 requests, 64q/8kv, 16-token pages, KV lengths U[qlen, 4096]:
+    4 drafted tokens (seed 1090), 16 (seed 1091; linear, or random draft
+    trees drawn after the batch) or 32-token draft trees (seed 1094)."""
+    qlen, seed, tree = {"verify_4tok": (4, 1090, False), "verify_16tok": (16, 1091, False),
+                        "verify_tree_16tok": (16, 1091, True),
+                        "verify_tree_32tok": (32, 1094, True)}[name]
+    rng = np.random.default_rng(seed)
+    L = rng.integers(qlen, 4096, size=64, endpoint=True)
+    kind = "draft trees" if tree else "drafted tokens"
+    b = make_batch(rng, kind="prefill", qlens=[qlen] * 64, kv_lens=L, hq=64, hkv=8, paged=True,
+                   sinks="normal",
+                   name=f"verify: B=64 x {qlen} {kind}, L~U[{qlen},4096], 64q/8kv, page 16")
+    if tree:
+        b.draft_mask = np.concatenate([tree_mask(draft_tree(rng, qlen)) for _ in range(64)])
+    return b
+
+
+def append_workload(name: str) -> AppendBatch:
+    """The bias + rotary + append step of 64q/8kv: a prefill step of 8 x 4096
+    new tokens, or a decode step of 64 requests x 1 token with KV lengths
+    U[1, 4096] (seed 1092); the projections and caches from seed 1093."""
+    if name == "append_prefill_8x4096":
+        qlens, kvl = [4096] * 8, [4096] * 8
+    elif name == "append_decode_64":
+        qlens, kvl = [1] * 64, list(np.random.default_rng(1092).integers(1, 4097, size=64))
+    else:
+        raise ValueError(name)
+    return make_append_batch(1093, qlens=qlens, kv_lens=kvl, hq=64, hkv=8, spare_pages=0,
+                             name=f"{sum(qlens)} new tokens, 64q/8kv, d=64, page 16, YaRN table")
