@@ -361,7 +361,7 @@ def cpu_baseline(b, kv_bytes, seconds):
         t = time.perf_counter()
         oracle.attend(b, nthreads=threads)
         times.append(time.perf_counter() - t)
-        if time.perf_counter() >= t_end or len(times) >= 50:
+        if time.perf_counter() >= t_end or len(times) >= 1000:
             break
     mean = float(np.mean(times))
     return dict(value=round(kv_bytes / mean / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
