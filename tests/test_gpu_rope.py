@@ -198,3 +198,27 @@ def test_tokens_outside_the_table_or_pages_are_skipped(case):
     _close(f"skip {case}: v", vp[new], rv[new])
     assert np.array_equal(kp[~new], ab.k_pages[~new])
     assert np.array_equal(vp[~new], ab.v_pages[~new])
+
+
+def test_append_many_and_empty_requests():
+    """Thousands of requests, nearly all empty: the rows of one workgroup lie
+    dozens of requests apart, so the request lookup takes its sampled first
+    level (batch > 64) and slides its window of 64 entries."""
+    rng = np.random.default_rng(63)
+    B = 5000
+    qlens = np.where(rng.random(B) < 0.97, 0, rng.integers(1, 4, size=B))
+    qlens[:2] = [0, 1]
+    qlens[-1] = 2
+    kvl = qlens + np.where(qlens > 0, rng.integers(0, 40, size=B), rng.integers(0, 3, size=B))
+    ab = W.make_append_batch(rng, qlens=qlens, kv_lens=kvl, hq=8, hkv=2, spare_pages=2)
+    max_pos = int(kvl.max())
+    q, kp, vp = _run_append(ab, _gpu_table(max_pos, YARN), max_pos, 0)
+    rq, rk, rv = rope.qkv_rope_append(ab.qkv, ab.bias, _ref_table(max_pos, YARN), ab.qo_indptr,
+                                      ab.kv_len, ab.page_indptr, ab.page_indices, ab.k_pages,
+                                      ab.v_pages, 8, 2, False)
+    _close("many requests q", q, rq)
+    new = _new_slots(ab, range(B), kvl)
+    _close("many requests k", kp[new], rk[new])
+    _close("many requests v", vp[new], rv[new])
+    assert np.array_equal(kp[~new], ab.k_pages[~new])
+    assert np.array_equal(vp[~new], ab.v_pages[~new])
