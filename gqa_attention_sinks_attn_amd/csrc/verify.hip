@@ -77,7 +77,7 @@ struct alignas(16) VerifySlot {
 };
 
 template <int G, int NB, bool TREE>
-__global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void verify_kernel(VerifyArgs p) {
   constexpr int kSlotBytes = (int)sizeof(VerifySlot<NB>);
   constexpr int kLdsBytes = (kWaves * kWaveLds * 2) > (kWaves * kSlotBytes)
                                 ? (kWaves * kWaveLds * 2) : (kWaves * kSlotBytes);
@@ -189,17 +189,26 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
     const bool two = (pp + 1) < pg1;
     // V rows past the request's last key (tail of its last page, or a
     // missing second page) are zeroed: 0 x an unwritten slot must stay 0.
+    // Only a step that reaches the end of the cache (or misses its second
+    // page) needs the selects: a wave-uniform branch.
     {
-      const int vkey = pp * kPage + (lane >> 2);
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const bool d0 = vkey >= L;
-      const bool d1 = !two || vkey + kPage >= L;
       uint16_t* r0 = my_v + (lane >> 2) * kVPitch + 16 * (lane & 3);
       uint16_t* r1 = r0 + kPage * kVPitch;
-      *reinterpret_cast<u32x4*>(r0) = d0 ? z : r.v00;
-      *reinterpret_cast<u32x4*>(r0 + 8) = d0 ? z : r.v01;
-      *reinterpret_cast<u32x4*>(r1) = d1 ? z : r.v10;
-      *reinterpret_cast<u32x4*>(r1 + 8) = d1 ? z : r.v11;
+      if (two && pp * kPage + 2 * kPage <= L) {
+        *reinterpret_cast<u32x4*>(r0) = r.v00;
+        *reinterpret_cast<u32x4*>(r0 + 8) = r.v01;
+        *reinterpret_cast<u32x4*>(r1) = r.v10;
+        *reinterpret_cast<u32x4*>(r1 + 8) = r.v11;
+      } else {
+        const int vkey = pp * kPage + (lane >> 2);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const bool d0 = vkey >= L;
+        const bool d1 = !two || vkey + kPage >= L;
+        *reinterpret_cast<u32x4*>(r0) = d0 ? z : r.v00;
+        *reinterpret_cast<u32x4*>(r0 + 8) = d0 ? z : r.v01;
+        *reinterpret_cast<u32x4*>(r1) = d1 ? z : r.v10;
+        *reinterpret_cast<u32x4*>(r1 + 8) = d1 ? z : r.v11;
+      }
     }
     // V^T operands of the step, one per 16-dim block, shared by every
     // column block: source lane s of group grp points at key 4 grp + s / 4,
@@ -216,6 +225,13 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
     // tree visibility, the end of the cache) or miss their second page.
     const bool edge = pp * kPage + 2 * kPage > P || !two;
     const bool draft = TREE && edge;
+    // The step runs in phases over all column blocks at once (scores,
+    // masks, exponentials, one slow-path test, P.V), so the matrix core and
+    // the vector unit always have independent work from the other block
+    // and a step has one mask branch and one slow-path branch.
+    // (1) S^T = K Q^T per block, K straight from registers; raw scores (the
+    //     scale is applied inside the exponent's FMA).
+    float sc[NB][8];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
@@ -223,13 +239,16 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
       s1 = mfma16(as_bf16x8(r.k10), bq0[blk], s1);
       s0 = mfma16(as_bf16x8(r.k01), bq1[blk], s0);
       s1 = mfma16(as_bf16x8(r.k11), bq1[blk], s1);
-      float sc[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sc[i] = s0[i] * p.scale_log2;
-        sc[4 + i] = s1[i] * p.scale_log2;
+        sc[blk][i] = s0[i];
+        sc[blk][4 + i] = s1[i];
       }
-      if (draft) {
+    }
+    // (2) Masks.
+    if (draft) {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
         // drafted key P + j is visible when bit j is set (j < qlen, so the
         // key also lies below kv_len)
         auto seen = [&](int key) -> bool {
@@ -240,49 +259,72 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyArgs p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int k0 = key_base + i, k1 = key_base + kPage + i;
-          if (!seen(k0)) sc[i] = -INFINITY;
-          if (!(seen(k1) && k1 < lim2)) sc[4 + i] = -INFINITY;
+          if (!seen(k0)) sc[blk][i] = -INFINITY;
+          if (!(seen(k1) && k1 < lim2)) sc[blk][4 + i] = -INFINITY;
         }
-      } else if (edge) {
+      }
+    } else if (edge) {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int k0 = key_base + i, k1 = key_base + kPage + i;
-          if (!(k0 <= lim[blk])) sc[i] = -INFINITY;
-          if (!(k1 <= lim[blk] && k1 < lim2)) sc[4 + i] = -INFINITY;
+          if (!(k0 <= lim[blk])) sc[blk][i] = -INFINITY;
+          if (!(k1 <= lim[blk] && k1 < lim2)) sc[blk][4 + i] = -INFINITY;
         }
-      }
-      // Exponentiate against the column's reference maximum m.  The fast
-      // path holds while every lane's partial sum stays below kFastLimit
-      // and the column has a reference; otherwise take the true maximum of
-      // the step, rescale d and O, and exponentiate again.  Either way the
-      // result is the online softmax's.
-      uint32_t pw[4];
-      float psum = 0.f;
-      auto expo = [&](float m_use) {
-        psum = 0.f;
+    }
+    // (3) Exponentiate against each column's reference maximum m:
+    //     exp2(s * scale - m), one FMA per score (a masked score gives 0).
+    //     The fast path holds while every lane's partial sum stays below
+    //     kFastLimit and the column has a reference; otherwise take the true
+    //     maximum of the step, rescale d and O, and exponentiate again.
+    //     Either way the result is the online softmax's.
+    uint32_t pw[NB][4];
+    float psum[NB];
+    const float sl2 = p.scale_log2;
+    auto expo = [&](int blk, float m_use) {
+      psum[blk] = 0.f;
+      const float nm = -m_use;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pw[i] = pack_bf16x2(fast_exp2(sc[2 * i] - m_use), fast_exp2(sc[2 * i + 1] - m_use));
-          psum = dot2_sum(pw[i], psum);
-        }
-      };
-      expo(m[blk]);
-      float alpha = 1.f;
-      if (__any(!(psum <= kFastLimit) || m[blk] == -INFINITY)) {
-        float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                         fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      for (int i = 0; i < 4; ++i) {
+        pw[blk][i] = pack_bf16x2(fast_exp2(__builtin_fmaf(sc[blk][2 * i], sl2, nm)),
+                                 fast_exp2(__builtin_fmaf(sc[blk][2 * i + 1], sl2, nm)));
+        psum[blk] = dot2_sum(pw[blk][i], psum[blk]);
+      }
+    };
+    bool slow = false;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      expo(blk, m[blk] == -INFINITY ? 0.f : m[blk]);
+      slow = slow || !(psum[blk] <= kFastLimit) || m[blk] == -INFINITY;
+    }
+    // (4) The slow path (rare; wave-uniform): the rescale of d and O
+    //     happens only here, so the fast path never touches the
+    //     accumulators outside the MFMA.
+    if (__any(slow)) {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        const float* x = sc[blk];
+        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         mx = fmaxf(mx, xor_lane(mx, 16));
         mx = fmaxf(mx, xor_lane(mx, 32));
-        const float m_new = fmaxf(m[blk], mx);
-        alpha = (m[blk] == m_new) ? 1.f : fast_exp2(m[blk] - m_new);
+        const float m_new = fmaxf(m[blk], mx * sl2);
+        const float alpha = (m[blk] == m_new) ? 1.f : fast_exp2(m[blk] - m_new);
         m[blk] = m_new;
-        expo(m_new == -INFINITY ? 0.f : m_new);
-      }
-      d[blk] = d[blk] * alpha + psum;
-      // P^T operand: slot j <-> key (j < 4 ? 4 grp + j : 16 + 4 grp + j - 4)
-      const bf16x8 pb = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+        d[blk] *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[blk][db] = mfma16(vt[db], pb, o[blk][db] * alpha);
+        for (int db = 0; db < 4; ++db) o[blk][db] *= alpha;
+        expo(blk, m_new == -INFINITY ? 0.f : m_new);
+      }
+    }
+    // (5) O^T += V^T P^T; P^T slot j <-> key (j < 4 ? 4 grp + j : 16 + 4 grp + j - 4)
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      d[blk] += psum[blk];
+      const bf16x8 pb = as_bf16x8(u32x4{pw[blk][0], pw[blk][1], pw[blk][2], pw[blk][3]});
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[blk][db] = mfma16(vt[db], pb, o[blk][db]);
     }
   };
 
