@@ -235,11 +235,11 @@ def bench_extra(args, torch, sa, device, W):
     verify_line("verify_4tok", vb, "sink_attn_verify (automatic split plan)")
     log("[bench] extra: tree verification batch")
     verify_line("verify_16tok_causal", W.verify_workload("verify_16tok"),
-                "sink_attn_verify (linear 16-token drafts, causal)")
+                "sink_attn_verify (linear 16-token drafts, causal; 128-row tiles)")
     verify_line("verify_tree_16tok", W.verify_workload("verify_tree_16tok"),
-                "sink_attn_verify_tree (one mask word per token)")
+                "sink_attn_verify_tree (one mask word per token; 128-row tiles)")
     verify_line("verify_tree_32tok", W.verify_workload("verify_tree_32tok"),
-                "sink_attn_verify_tree (automatic plan: prefill tiles)")
+                "sink_attn_verify_tree (automatic plan: 128-row tiles)")
     log("[bench] extra: bias + rotary + paged append")
     append_lines(args, torch, sa, W, res, steps, warm)
     log("[bench] extra: decode step, eager and as a captured graph")

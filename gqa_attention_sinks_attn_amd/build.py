@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsink_attn.so")
 SOURCES = ["api.cpp", "decode.hip", "decode_balanced.hip", "merge.hip", "prefill.hip",
-           "rope_append.hip", "verify.hip"]
+           "rope_append.hip", "verify.hip", "verify_tile.hip"]
 ARCH = "gfx950"
 
 

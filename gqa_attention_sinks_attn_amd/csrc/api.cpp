@@ -594,19 +594,63 @@ int32_t verify_column_groups(int32_t columns) {
 // sink_attn_decode takes it.
 constexpr int64_t kVerifyTargetWorkgroups = 512;
 
-// Wide drafts under the automatic plan run the prefill kernel instead: its
-// 256-row tiles on 32x32 MFMAs, K/V staged in LDS once per workgroup, beat
-// column groups on 16x16 MFMAs past 128 (token, head) pairs per KV head
-// (measured: 4 groups at 16 tokens x G = 8 tie, 8 groups at 32 tokens lose
-// ~1.8x).  Group sizes the prefill kernel is built for only.
-bool verify_uses_prefill(int32_t group, int32_t columns, int32_t requested) {
-  return requested == 0 && columns > 128 && (group == 1 || group == 2 || group == 4 || group == 8);
+// Wide drafts, more than kVerifyTileMinColumns (token, head) pairs per KV
+// head, run the tile kernel (verify_tile.hip): 128-row tiles on 32x32 MFMAs
+// with each K/V tile staged in LDS once per workgroup, where column groups
+// on 16x16 MFMAs would read every page once per group.  Group sizes the
+// tile kernel is built for only.
+constexpr int32_t kVerifyTileMinColumns = 64;
+constexpr int32_t kVerifyTileRows = 128;
+constexpr int32_t kVerifyTileKeys = 64;
+constexpr int32_t kVerifyTileMaxChunks = 64;
+// Automatic chunking of the tile kernel: one chunk per request while the
+// (request, KV head, row tile) units alone give kVerifyTileTargetWorkgroups
+// workgroups (two per CU); below that, enough chunks of at least 8 tiles
+// (512 keys) to reach it.  Chunks cost partial writes and a merge pass
+// (measured on 64 requests x 16 tokens, L <= 4,096, 512 units: first pass
+// 96 us in one chunk, 79 us in two, plus 24 us of merge), so a grid that
+// already fills the GPU is not split.
+constexpr int64_t kVerifyTileTargetWorkgroups = 512;
+constexpr int32_t kVerifyTileMinChunkTiles = 8;
+
+bool verify_uses_tiles(int32_t group, int32_t columns) {
+  return columns > kVerifyTileMinColumns &&
+         (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
+}
+
+struct TilePlan {
+  int32_t row_tiles, chunk_tiles, chunks;
+};
+
+TilePlan verify_tile_plan(int32_t batch, int32_t hkv, int32_t columns, int32_t max_kv_len,
+                          int32_t requested) {
+  TilePlan tp;
+  tp.row_tiles = (columns + kVerifyTileRows - 1) / kVerifyTileRows;
+  const int32_t tiles = max_kv_len > 0 ? (max_kv_len + kVerifyTileKeys - 1) / kVerifyTileKeys : 1;
+  int64_t want;   // chunks per request of max_kv_len keys
+  if (requested > 0) {
+    want = requested;
+  } else {
+    const int64_t units = (int64_t)batch * hkv * tp.row_tiles;
+    want = units > 0 ? (kVerifyTileTargetWorkgroups + units - 1) / units : 1;
+    const int64_t by_len = tiles / kVerifyTileMinChunkTiles;
+    if (want > by_len) want = by_len;
+  }
+  if (want < 1) want = 1;
+  if (want > tiles) want = tiles;
+  int32_t ct = (int32_t)((tiles + want - 1) / want);
+  const int32_t min_ct = (tiles + kVerifyTileMaxChunks - 1) / kVerifyTileMaxChunks;
+  if (ct < min_ct) ct = min_ct;
+  tp.chunk_tiles = ct;
+  tp.chunks = (tiles + ct - 1) / ct;
+  return tp;
 }
 
 int32_t verify_plan_splits(int32_t batch, int32_t hkv, int32_t columns, int32_t max_kv_len,
                            int32_t requested, int32_t group) {
+  if (verify_uses_tiles(group, columns))
+    return verify_tile_plan(batch, hkv, columns, max_kv_len, requested).chunks;
   if (requested > 0) return plan_splits(batch, hkv, max_kv_len, requested);
-  if (verify_uses_prefill(group, columns, requested)) return 1;
   const int32_t pages = (max_kv_len + kPageSize - 1) / kPageSize;
   const int64_t units = (int64_t)batch * hkv * verify_column_groups(columns);
   if (units <= 0 || units * 2 >= kVerifyTargetWorkgroups || pages <= 16) return 1;
@@ -689,28 +733,39 @@ sink_attn_status verify_impl(const void* q, const int32_t* qo_indptr, const void
   }
   if (total_q == 0 || max_qlen == 0) return ok();
 
-  if (verify_uses_prefill(G, max_qlen * G, num_splits)) {
-    sa::PrefillArgs pa;
-    pa.q = static_cast<const uint16_t*>(q);
-    pa.qo_indptr = qo_indptr;
-    pa.k = static_cast<const uint16_t*>(k_pages);
-    pa.v = static_cast<const uint16_t*>(v_pages);
-    pa.kv_indptr = page_indptr;
-    pa.page_indices = page_indices;
-    pa.kv_len = kv_len;
-    pa.sinks = sinks;
-    pa.batch = batch;
-    pa.hq = num_qo_heads;
-    pa.hkv = num_kv_heads;
-    pa.max_qlen = max_qlen;
-    pa.causal = 1;
-    pa.scale_log2 = sm_scale * 1.4426950408889634f;
-    pa.out = out;
-    pa.out_f32 = out_dtype == SINK_ATTN_F32;
-    pa.lse = lse;
-    pa.draft_mask = draft_mask;
-    return hip_status(sa::launch_prefill(pa, G, static_cast<hipStream_t>(stream)),
-                      "verify (prefill tiles) launch");
+  if (verify_uses_tiles(G, max_qlen * G)) {
+    const TilePlan tp = verify_tile_plan(batch, num_kv_heads, max_qlen * G, max_kv_len, num_splits);
+    sa::VerifyTileArgs ta;
+    ta.q = static_cast<const uint16_t*>(q);
+    ta.qo_indptr = qo_indptr;
+    ta.k = static_cast<const uint16_t*>(k_pages);
+    ta.v = static_cast<const uint16_t*>(v_pages);
+    ta.page_indptr = page_indptr;
+    ta.page_indices = page_indices;
+    ta.kv_len = kv_len;
+    ta.sinks = sinks;
+    ta.draft_mask = draft_mask;
+    ta.batch = batch;
+    ta.hq = num_qo_heads;
+    ta.hkv = num_kv_heads;
+    ta.max_qlen = max_qlen;
+    ta.row_tiles = tp.row_tiles;
+    ta.chunk_tiles = tp.chunk_tiles;
+    ta.max_chunks = tp.chunks;
+    ta.scale_log2 = sm_scale * 1.4426950408889634f;
+    ta.out = out;
+    ta.out_f32 = out_dtype == SINK_ATTN_F32;
+    ta.lse = lse;
+    ta.o_part = nullptr;
+    ta.lse_part = nullptr;
+    if (tp.chunks > 1) {
+      ta.o_part = static_cast<float*>(workspace);
+      ta.lse_part = reinterpret_cast<float*>(
+          static_cast<char*>(workspace) +
+          (size_t)total_q * num_qo_heads * tp.chunks * head_dim * sizeof(float));
+    }
+    return hip_status(sa::launch_verify_tile(ta, G, static_cast<hipStream_t>(stream)),
+                      "verify (tiles) launch");
   }
 
   sa::VerifyArgs a;

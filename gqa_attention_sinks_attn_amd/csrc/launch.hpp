@@ -69,6 +69,29 @@ struct VerifyArgs {
   int32_t col_groups;           // Z: groups of 64 (token, head) columns per (request, KV head)
 };
 
+struct VerifyTileArgs {
+  const uint16_t* q;            // bf16 [total_q, Hq, 64]
+  const int32_t* qo_indptr;     // [B+1]
+  const uint16_t* k;            // bf16 [num_pages, Hkv, 16, 64]
+  const uint16_t* v;
+  const int32_t* page_indptr;   // [B+1]
+  const int32_t* page_indices;  // [nnz]
+  const int32_t* kv_len;        // [B]
+  const float* sinks;           // [Hq] or nullptr
+  const uint64_t* draft_mask;   // [total_q] drafted-token visibility, or nullptr (causal)
+  int32_t batch, hq, hkv;
+  int32_t max_qlen;             // upper bound of qlen_b (finish grid)
+  int32_t row_tiles;            // 128-row tiles per (request, KV head)
+  int32_t chunk_tiles;          // 64-key tiles per KV chunk
+  int32_t max_chunks;           // chunks of the longest request (<= 64)
+  float scale_log2;             // sm_scale * log2(e)
+  void* out;                    // [total_q, Hq, 64]
+  int32_t out_f32;
+  float* lse;                   // [total_q, Hq] or nullptr
+  float* o_part;                // [total_q, Hq, max_chunks, 64] (max_chunks > 1)
+  float* lse_part;              // [total_q, Hq, max_chunks]
+};
+
 struct MergeArgs {
   const float* o_parts;         // [N, H, S, 64]
   const float* lse_parts;       // [N, H, S] natural log
@@ -123,6 +146,7 @@ struct RopeAppendArgs {
 };
 
 hipError_t launch_verify(const VerifyArgs& a, int group, int column_blocks, hipStream_t stream);
+hipError_t launch_verify_tile(const VerifyTileArgs& a, int group, hipStream_t stream);
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t stream);
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);

@@ -1,0 +1,494 @@
+// Wide drafted-token verification with a per-head sink (gfx950): the
+// drafted tokens x query heads of a request form up to 128-row tiles that
+// stream its paged KV cache through LDS, split along the KV length.
+//
+// GPT-OSS on Day 0 (Perplexity), "Sink attention" under "Kernels for
+// GPT-OSS": the sink is an extra logit per head, folded into the online
+// softmax by starting the running maximum at the sink with d = 1; work is
+// parallel over heads and along the KV length, and when the KV sequence is
+// split only the first chunk carries the sink.  "Accelerating Sonar Through
+// Speculation" (Perplexity), "Speculative Decoding" and "MTP": the target
+// model runs once over each request's drafted tokens; "EAGLE": tree drafts
+// are checked under custom attention masks.
+//
+// One workgroup = (request b, KV head g, KV chunk c, row tile rt), four
+// waves.  Row rho = 128 rt + 32 w + (lane % 32) of wave w is drafted token
+// t = rho / G with query head g G + rho % G; rows past qlen_b G are padding.
+// Token t sits at position P + t, P = kv_len - qlen, and sees keys 0 .. P + t
+// (bottom-right causal alignment), or, with a draft mask, every key below P
+// plus drafted key P + i when bit i of its word is set.
+//
+// Chunk c covers the 64-key tiles c Ct .. c Ct + Ct - 1 of the request.  The
+// workgroup stages each tile's K and V in LDS once (double-buffered, the
+// next tile's page ids and rows in flight), and every wave computes on it:
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 for the tile's two 32-key
+//     halves, so a lane holds 16 scores of one row per half;
+//   * the halves are interleaved: the scores of half 1 are computed while
+//     half 0 is exponentiated, and O^T += V^T P^T of half 0 runs while half
+//     1 is exponentiated (V^T read transposed with ds_read_b64_tr_b16 in
+//     the key order of the score layout, P^T straight from registers);
+//   * softmax against a per-row reference maximum: exp2(s scale - m) with
+//     one FMA; only when a lane's partial sum of a half passes 2^15, or the
+//     row has no reference yet, does a wave-uniform slow path take the true
+//     maximum and rescale d and O;
+//   * masks run only on tiles that reach the drafted keys or the end of
+//     the cache.
+// A request that fits in one chunk writes its rows; a longer one writes a
+// normalised partial (o, lse) per chunk, which verify_tile_finish merges.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace sa {
+namespace {
+
+constexpr int kD = 64;
+constexpr int kTile = 64;             // keys per tile
+constexpr int kRows = 128;            // rows per workgroup (4 waves x 32)
+constexpr int kKPitch = 72;           // K tile row pitch in bf16 (144 B)
+constexpr int kVPitch = 80;           // V tile row pitch in bf16 (160 B)
+constexpr int kKBuf = kTile * kKPitch;
+constexpr int kVBuf = kTile * kVPitch;
+constexpr float kFastLimit = 32768.f; // lane-partial half-tile sum that forces a rescale
+
+// acc + lo(w) + hi(w) for a packed bf16 pair, accumulated in fp32.
+__device__ __forceinline__ float dot2_sum(uint32_t w, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
+__device__ __forceinline__ int n_chunks_of(int L, int chunk_tiles) {
+  const int tiles = (L + kTile - 1) / kTile;
+  return (tiles + chunk_tiles - 1) / chunk_tiles;
+}
+
+template <int G, bool TREE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void verify_tile_kernel(VerifyTileArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * kKBuf];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * kVBuf];
+
+  // flat index -> (work item = c * B * Hkv + unit, row tile rt): the row
+  // tiles of one item go to the same XCD (workgroups are dealt to the 8 XCDs
+  // round robin), back to back, so their reads of the same pages meet in
+  // that XCD's L2.
+  const int n_units = p.batch * p.hkv;
+  const int xcd = block_x() & 7;
+  const int rest = block_x() >> 3;
+  const int rt = rest % p.row_tiles;
+  const int item = (rest / p.row_tiles) * 8 + xcd;
+  if (item >= n_units * p.max_chunks) return;
+  const int unit = item % n_units;
+  const int c = item / n_units;
+  const int g = unit % p.hkv;
+  const int b = unit / p.hkv;
+
+  const int q0 = p.qo_indptr[b];
+  const int qlen = p.qo_indptr[b + 1] - q0;
+  const int n_rows = qlen * G;
+  if (kRows * rt >= n_rows) return;
+  const int L = p.kv_len[b];
+  const int n_chunks = n_chunks_of(L, p.chunk_tiles);
+  if (c >= n_chunks) return;
+  const int n_tiles_all = (L + kTile - 1) / kTile;
+  const int tile0 = c * p.chunk_tiles;
+  const int n_tiles = min(n_tiles_all - tile0, p.chunk_tiles);
+  const int P = L - qlen;          // keys below P: the cached prefix
+  const int kv_start = p.page_indptr[b];
+
+  const int tid = thread_x();
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 31;
+  const int hh = lane >> 5;
+
+  // ---- this lane's row ----
+  const int rho = kRows * rt + 32 * wave + r;
+  const bool valid = rho < n_rows;
+  const int t = valid ? rho / G : 0;
+  const int head = g * G + rho % G;
+  bf16x8 bq[4];
+  {
+    const uint16_t* qrow = p.q + ((int64_t)(q0 + t) * p.hq + head) * kD + 8 * hh;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) bq[s] = as_bf16x8(valid ? ld16(qrow + 16 * s) : z);
+  }
+  uint32_t mlo = 0u, mhi = 0u;
+  if (TREE && valid) {
+    const uint64_t w = p.draft_mask[q0 + t];
+    mlo = (uint32_t)w;
+    mhi = (uint32_t)(w >> 32);
+  }
+  // causal limit of the row: keys <= lim are visible
+  const int lim = P + t;
+
+  // ---- online state (log2 units); chunk 0 starts at the sink.  Padding
+  // rows get a finite reference, so they never take the slow path. ----
+  float m = valid ? -INFINITY : 0.f;
+  float d = 0.f;
+  if (valid && c == 0 && p.sinks != nullptr) {
+    const float sg = p.sinks[head];
+    m = sg * kLog2e;
+    d = (hh == 0 && sg != -INFINITY) ? 1.f : 0.f;
+  }
+  f32x16 o[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
+
+  // ---- tile loader: thread -> rows ld_row and 32 + ld_row, one 16 B chunk.
+  // Loads are unconditional: tiles past the chunk repeat its last tile, and
+  // rows past the last key read key 0 (their V rows are zeroed when stored,
+  // their scores masked: every tile holding them is an edge tile). ----
+  const int ld_row = tid >> 3;
+  const int ld_chunk = tid & 7;
+  const int64_t head_stride = (int64_t)16 * kD;
+  const int64_t page_stride = (int64_t)p.hkv * head_stride;
+  const int64_t vdelta = p.v - p.k;
+  u32x4 rk0, rk1, rv0, rv1;
+  int id_a = 0, id_b = 0;
+  auto tile_key0 = [&](int kt) { return (tile0 + min(kt, n_tiles - 1)) * kTile; };
+  auto load_ids = [&](int kt) {
+    const int key0 = tile_key0(kt);
+    const int ka = key0 + ld_row, kb2 = key0 + 32 + ld_row;
+    id_a = p.page_indices[kv_start + ((ka < L ? ka : 0) >> 4)];
+    id_b = p.page_indices[kv_start + ((kb2 < L ? kb2 : 0) >> 4)];
+  };
+  auto load_tile = [&](int kt) {
+    const int key0 = tile_key0(kt);
+    const int ka = key0 + ld_row, kb2 = key0 + 32 + ld_row;
+    const uint16_t* pa = p.k + id_a * page_stride + g * head_stride +
+                         ((ka < L ? ka : 0) & 15) * kD + 8 * ld_chunk;
+    const uint16_t* pb = p.k + id_b * page_stride + g * head_stride +
+                         ((kb2 < L ? kb2 : 0) & 15) * kD + 8 * ld_chunk;
+    rk0 = ld16(pa);
+    rk1 = ld16(pb);
+    rv0 = ld16(pa + vdelta);
+    rv1 = ld16(pb + vdelta);
+  };
+  auto store_tile = [&](int buf, int kt) {
+    const int key0 = tile_key0(kt);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    uint16_t* kd = lds_k + buf * kKBuf;
+    uint16_t* vd = lds_v + buf * kVBuf;
+    *reinterpret_cast<u32x4*>(kd + ld_row * kKPitch + 8 * ld_chunk) = rk0;
+    *reinterpret_cast<u32x4*>(kd + (32 + ld_row) * kKPitch + 8 * ld_chunk) = rk1;
+    *reinterpret_cast<u32x4*>(vd + ld_row * kVPitch + 8 * ld_chunk) = key0 + ld_row < L ? rv0 : z;
+    *reinterpret_cast<u32x4*>(vd + (32 + ld_row) * kVPitch + 8 * ld_chunk) =
+        key0 + 32 + ld_row < L ? rv1 : z;
+  };
+
+  load_ids(0);
+  load_tile(0);
+  load_ids(1);
+  store_tile(0, 0);
+  __syncthreads();
+
+  const float sl2 = p.scale_log2;
+  // transposed V reads: 16-lane group q = lane / 16 covers dims 16 (q % 2) ..
+  // of a 32-dim block and keys 4 hh + s / 4 (s = lane % 16)
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int buf = kt & 1;
+    load_tile(kt + 1);   // clamped: the last iteration repeats the last tile
+    load_ids(kt + 2);
+    const int key0 = (tile0 + kt) * kTile;
+    const uint16_t* kbuf = lds_k + buf * kKBuf;
+    const uint16_t* vbuf = lds_v + buf * kVBuf;
+    // tiles that reach the drafted keys (from P) or the end of the cache
+    const bool edge = key0 + kTile > P;
+    const f32x16 zero16 = {};
+
+    // K operand (A of S^T) for k-step s, half kb: keys 32 kb + r, dims
+    // 16 s + 8 hh.  V^T operand (A of O^T) for half kb, k-step hf, dim
+    // block db: dims 32 db + .., keys 32 kb + 16 hf + {4 hh .., 8 + 4 hh ..}.
+    auto kop = [&](int s, int kb) {
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(kbuf + (32 * kb + r) * kKPitch + 16 * s + 8 * hh));
+    };
+    auto vop = [&](int kb, int hf, int db) {
+      const uint16_t* src = vbuf + (32 * kb + 16 * hf + tr_row) * kVPitch + tr_col + 32 * db;
+      return as_bf16x8(lds_tr16_pair(src, src + 8 * kVPitch));
+    };
+    // S^T[kb]: keys 32 kb + 8 (j / 4) + 4 hh + j % 4, column = this row
+    f32x16 sacc[2];
+    uint32_t pk[2][2][4];   // [kb][hf][pair]
+    auto mask = [&](int kb) {
+      if (TREE) {
+        // draft index of the key at offset 32 kb + 8 (j / 4) + j % 4 +
+        // 4 hh: below 0 a prefix key (seen), from qlen on past the cache
+        int base = key0 + 32 * kb + 4 * hh - P;
+        asm volatile("" : "+v"(base));
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int jj = base + 8 * (j >> 2) + (j & 3);
+          const uint32_t w = jj < 32 ? mlo : mhi;
+          const bool seen = jj < 0 || (jj < qlen && ((w >> (jj & 31)) & 1u));
+          if (!seen) sacc[kb][j] = -INFINITY;
+        }
+        return;
+      }
+      int rel = lim - key0 - 32 * kb - 4 * hh;
+      // defined here, so the compares cannot be hoisted out of the (rare)
+      // edge branch into every tile
+      asm volatile("" : "+v"(rel));
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (8 * (j >> 2) + (j & 3) > rel) sacc[kb][j] = -INFINITY;
+    };
+    // exp2(s * scale - m) of scores j = 8 hf + 2 q, + 1 of half kb, packed;
+    // the row sum adds the rounded values the MFMA consumes.
+    auto expo2 = [&](float neg_m, int kb, int hf, int q, float& acc) {
+      const int j = 8 * hf + 2 * q;
+      const float e0 = fast_exp2(__builtin_fmaf(sacc[kb][j], sl2, neg_m));
+      const float e1 = fast_exp2(__builtin_fmaf(sacc[kb][j + 1], sl2, neg_m));
+      const uint32_t w = pack_bf16x2(e0, e1);
+      pk[kb][hf][q] = w;
+      acc = dot2_sum(w, acc);
+    };
+    auto neg_ref = [&]() { return (m == -INFINITY) ? 0.f : -m; };
+    // Fast path: half kb was exponentiated against the reference m.  It is
+    // valid while every partial sum stays below 2^15 and the row has a
+    // reference; otherwise take the half's true maximum, rescale O, d and
+    // m, and exponentiate again.
+    auto settle = [&](int kb, float ds) {
+      if (__any(!(ds <= kFastLimit) || m == -INFINITY)) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) mx = fmaxf(fmaxf(mx, sacc[kb][j]), sacc[kb][j + 1]);
+        mx = fmaxf(mx, xor_lane(mx, 32));
+        const float m_new = fmaxf(m, mx * sl2);
+        const float alpha = (m == m_new) ? 1.f : fast_exp2(m - m_new);
+        d *= alpha;
+        o[0] *= alpha;
+        o[1] *= alpha;
+        m = m_new;
+        float a0 = 0.f, a1 = 0.f;
+        const float nm = neg_ref();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) expo2(nm, kb, i >> 2, i & 3, (i & 1) ? a1 : a0);
+        ds = a0 + a1;
+      }
+      d += ds;
+    };
+    auto pb_of = [&](int kb, int hf) {
+      return as_bf16x8(u32x4{pk[kb][hf][0], pk[kb][hf][1], pk[kb][hf][2], pk[kb][hf][3]});
+    };
+
+    // (1) S^T of half 0; the K operands of both halves are read once.
+    bf16x8 ko[4][2];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) ko[s][kb] = kop(s, kb);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sacc[0] = mfma32(ko[s][0], bq[s], s == 0 ? zero16 : sacc[0]);
+    if (edge) mask(0);
+    // (2) S^T of half 1 on the matrix core while half 0 is exponentiated.
+    {
+      float a0 = 0.f, a1 = 0.f;
+      const float nm = neg_ref();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if ((i & 1) == 0) sacc[1] = mfma32(ko[i >> 1][1], bq[i >> 1], i == 0 ? zero16 : sacc[1]);
+        expo2(nm, 0, i >> 2, i & 3, (i & 1) ? a1 : a0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
+      }
+      settle(0, a0 + a1);
+    }
+    if (edge) mask(1);
+    // (3) O^T += V^T P^T of half 0 while half 1 is exponentiated.  The V^T
+    //     operands of the tile are read once, at the start.
+    bf16x8 vo[2][2][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vo[i >> 2][(i >> 1) & 1][i & 1] = vop(i >> 2, (i >> 1) & 1, i & 1);
+    {
+      float a0 = 0.f, a1 = 0.f;
+      const float nm = neg_ref();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if ((i & 1) == 0) {
+          const int hf = i >> 2, db = (i >> 1) & 1;
+          o[db] = mfma32(vo[0][hf][db], pb_of(0, hf), o[db]);
+        }
+        expo2(nm, 1, i >> 2, i & 3, (i & 1) ? a1 : a0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);    // DS read: all of V^T
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);     // VALU
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // VALU
+      }
+      settle(1, a0 + a1);
+    }
+    // (4) O^T += V^T P^T of half 1.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hf = i >> 1, db = i & 1;
+      o[db] = mfma32(vo[1][hf][db], pb_of(1, hf), o[db]);
+    }
+    store_tile(buf ^ 1, kt + 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: o = O / d, lse = m + log2 d (natural log at the boundary) ----
+  const float dt = d + xor_lane(d, 32);
+  if (!valid) return;
+  const float inv = dt > 0.f ? 1.f / dt : 0.f;
+  const float lse2 = dt > 0.f ? m + __builtin_amdgcn_logf(dt) : -INFINITY;
+  const int64_t pair = (int64_t)(q0 + t) * p.hq + head;
+  if (n_chunks == 1) {
+    const int64_t orow = pair * kD;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int dim = 32 * db + 8 * a + 4 * hh;
+        const float x0 = o[db][4 * a + 0] * inv, x1 = o[db][4 * a + 1] * inv;
+        const float x2 = o[db][4 * a + 2] * inv, x3 = o[db][4 * a + 3] * inv;
+        if (p.out_f32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + orow + dim) =
+              f32x4{x0, x1, x2, x3};
+        } else {
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + orow + dim) =
+              u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+        }
+      }
+    if (p.lse != nullptr && hh == 0) p.lse[pair] = lse2 * kLn2;
+  } else {
+    const int64_t slot = pair * p.max_chunks + c;
+    float* op = p.o_part + slot * kD;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int dim = 32 * db + 8 * a + 4 * hh;
+        *reinterpret_cast<f32x4*>(op + dim) =
+            f32x4{o[db][4 * a] * inv, o[db][4 * a + 1] * inv, o[db][4 * a + 2] * inv,
+                  o[db][4 * a + 3] * inv};
+      }
+    if (hh == 0) p.lse_part[slot] = lse2 * kLn2;
+  }
+}
+
+// One wave per (request, drafted token, query head), lane = dim: merges the
+// n > 1 chunk partials of a request that spans several chunks by
+// log-sum-exp (L = max lse_c, w_c = e^(lse_c - L), o = sum w_c o_c / sum w_c,
+// lse = L + ln sum w_c).  Requests in one chunk were written by the first
+// pass.  Every lane reads the same log-sum-exps (one transaction each) and
+// its own dim of the partial rows, eight chunks per batch, all loads of a
+// batch in flight together: no cross-lane traffic, one round trip after
+// the request's metadata for up to eight chunks.
+__global__ __launch_bounds__(256) void verify_tile_finish_kernel(VerifyTileArgs p) {
+  constexpr int kBatch = 8;
+  const int lane = thread_x() & 63;
+  const int64_t idx = (int64_t)block_x() * 4 + __builtin_amdgcn_readfirstlane(thread_x() >> 6);
+  const int64_t per_b = (int64_t)p.max_qlen * p.hq;
+  if (idx >= (int64_t)p.batch * per_b) return;
+  const int b = (int)(idx / per_b);
+  const int t = (int)((idx % per_b) / p.hq);
+  const int h = (int)(idx % p.hq);
+  const int q0 = __builtin_amdgcn_readfirstlane(p.qo_indptr[b]);
+  const int qlen = __builtin_amdgcn_readfirstlane(p.qo_indptr[b + 1]) - q0;
+  if (t >= qlen) return;
+  const int n = n_chunks_of(__builtin_amdgcn_readfirstlane(p.kv_len[b]), p.chunk_tiles);
+  if (n <= 1) return;
+  const int64_t pair = (int64_t)(q0 + t) * p.hq + h;
+  const float* ls = p.lse_part + pair * p.max_chunks;
+  const float* os = p.o_part + pair * p.max_chunks * kD + lane;
+
+  // the first batch: log-sum-exps and rows together (indices clamped; the
+  // extra slots repeat chunk n - 1 and weigh nothing)
+  float lv[kBatch], ov[kBatch];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const int cj = min(j, n - 1);
+    lv[j] = ls[cj];
+    ov[j] = os[(int64_t)cj * kD];
+  }
+  float Lm = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) Lm = fmaxf(Lm, lv[j]);
+  for (int c0 = kBatch; c0 < n; c0 += kBatch) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) Lm = fmaxf(Lm, ls[min(c0 + j, n - 1)]);
+  }
+  auto weight = [&](float lc) {
+    if (Lm == -INFINITY) return 0.f;
+    if (Lm == INFINITY) return lc == INFINITY ? 1.f : 0.f;
+    return __expf(lc - Lm);
+  };
+  float den = 0.f, acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const float w = j < n ? weight(lv[j]) : 0.f;
+    den += w;
+    acc += w != 0.f ? w * ov[j] : 0.f;
+  }
+  for (int c0 = kBatch; c0 < n; c0 += kBatch) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int cj = min(c0 + j, n - 1);
+      lv[j] = ls[cj];
+      ov[j] = os[(int64_t)cj * kD];
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float w = c0 + j < n ? weight(lv[j]) : 0.f;
+      den += w;
+      acc += w != 0.f ? w * ov[j] : 0.f;
+    }
+  }
+  const float o = den > 0.f ? acc / den : 0.f;
+  const int64_t dst = pair * kD + lane;
+  if (p.out_f32) reinterpret_cast<float*>(p.out)[dst] = o;
+  else reinterpret_cast<uint16_t*>(p.out)[dst] = float_to_bf16_bits(o);
+  if (p.lse != nullptr && lane == 0) {
+    float l;
+    if (Lm == -INFINITY) l = -INFINITY;
+    else if (Lm == INFINITY) l = INFINITY;
+    else l = Lm + __logf(den);
+    p.lse[pair] = l;
+  }
+}
+
+template <int G>
+hipError_t launch_g(const VerifyTileArgs& a, hipStream_t stream) {
+  const int64_t items = (int64_t)a.batch * a.hkv * a.max_chunks;
+  const int64_t wgs = ((items + 7) / 8) * 8 * a.row_tiles;
+  if (wgs == 0) return hipSuccess;
+  if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (a.draft_mask != nullptr)
+    hipLaunchKernelGGL((verify_tile_kernel<G, true>), dim3((unsigned)wgs), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((verify_tile_kernel<G, false>), dim3((unsigned)wgs), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_chunks == 1) return e;
+  const int64_t waves = (int64_t)a.batch * a.max_qlen * a.hq;
+  if (waves == 0) return hipSuccess;
+  hipLaunchKernelGGL(verify_tile_finish_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_verify_tile(const VerifyTileArgs& a, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_g<1>(a, stream);
+    case 2: return launch_g<2>(a, stream);
+    case 4: return launch_g<4>(a, stream);
+    case 8: return launch_g<8>(a, stream);
+    case 16: return launch_g<16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sa

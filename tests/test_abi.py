@@ -363,15 +363,25 @@ def test_verify_plan_and_workspace():
     assert sa.sink_attn_verify_workspace_size(64, 64, 8, 64, 256, 4, 4096, 0) == 0
     # 8 requests: 64 (request, KV head) pairs x 1 column group -> 8 chunks
     assert nsp(8, 64, 8, 4, 4096, 0) == 8
-    # 8-token drafts at G = 8: 64 pairs = 2 groups of 32 -> 4 chunks; at 16
-    # tokens the 4 groups already give 256 workgroups -> 1 chunk
+    # 8-token drafts at G = 8: 64 pairs = 2 groups of 32 -> 4 chunks
     assert nsp(8, 64, 8, 8, 4096, 0) == 4
-    assert nsp(8, 64, 8, 16, 4096, 0) == 1
-    # past 128 pairs per KV head the automatic plan runs prefill tiles: no split
-    assert nsp(2, 64, 8, 32, 4096, 0) == 1
-    assert sa.sink_attn_verify_workspace_size(2, 64, 8, 64, 64, 32, 4096, 0) == 0
-    # ... for the group sizes the prefill kernel has (G = 16 keeps column groups)
-    assert nsp(2, 64, 4, 32, 4096, 0) == 4
+    # past 64 pairs per KV head the tile kernel runs: 128-row tiles, one
+    # chunk when (request, KV head, row tile) units reach 512 workgroups ...
+    assert nsp(64, 64, 8, 16, 4096, 0) == 1
+    assert sa.sink_attn_verify_workspace_size(64, 64, 8, 64, 1024, 16, 4096, 0) == 0
+    assert nsp(32, 64, 8, 32, 4096, 0) == 1          # 2 row tiles x 256 units
+    # ... else chunks of >= 8 tiles (512 keys) towards 512 workgroups
+    assert nsp(8, 64, 8, 16, 4096, 0) == 8           # 64 units, 64 tiles
+    assert nsp(2, 64, 8, 32, 4096, 0) == 8           # 32 units (2 row tiles)
+    assert nsp(2, 64, 4, 32, 4096, 0) == 8           # G = 16: 4 row tiles, 32 units
+    assert nsp(8, 64, 8, 16, 300, 0) == 1            # 5 tiles: too short to split
+    assert nsp(2, 64, 8, 16, 131072, 0) == 32        # 16 units -> 32 chunks of 64 tiles
+    # at most 64 chunks: an explicit request is capped there
+    assert nsp(1, 64, 8, 16, 131072, 1000) == 64
+    S = nsp(2, 64, 8, 32, 4096, 0)
+    rows = 64 * 64 * S
+    assert sa.sink_attn_verify_workspace_size(2, 64, 8, 64, 64, 32, 4096, 0) == \
+        rows * 64 * 4 + ((rows * 4 + 255) // 256) * 256
     # nothing to compute (no rows, no requests) plans one chunk
     assert nsp(8, 64, 8, 0, 4096, 0) == 1 and nsp(0, 64, 8, 4, 4096, 0) == 1
     # chunks keep >= 16 pages; short caches are not split

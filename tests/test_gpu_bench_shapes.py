@@ -1,6 +1,6 @@
 """Parity at the exact batches `bench.py --extra` times, in the launch
 configuration it times them: the verification batches (automatic plan,
-which puts the 32-token trees on prefill tiles) against the attention
+which puts the 16- and 32-token drafts on the tile kernel) against the attention
 oracle in full, and the bias + rotary + append steps against the rope
 oracle (in full for the decode step, on sampled tokens for the 32,768-token
 prefill step).  Bars as in test_gpu_parity.py and test_gpu_rope.py.

@@ -4,8 +4,10 @@ and attends causally within them and to its whole prefix -- the same
 operation as a chunked prefill at a small qlen (bottom-right alignment:
 drafted token t sits at kv_len - qlen + t).  Through both sink_attn_prefill
 and the dedicated sink_attn_verify (split-KV plans S = 0 (automatic), 1, 3,
-64; drafts wider than 64 (token, head) pairs run several column groups),
-against the oracle, at the parity bar of the other GPU tests.
+64), against the oracle, at the parity bar of the other GPU tests.  Drafts
+of up to 64 (token, head) pairs per KV head run the column-group kernel
+(verify.hip); wider ones run the tile kernel (verify_tile.hip): the qlen 16,
+33, 40 and 64 cases below, and the dedicated tile tests.
 
 Tree drafts go through sink_attn_verify_tree: random trees in breadth-first
 order, one uint64 visibility word per drafted token, against the oracle's
@@ -175,10 +177,47 @@ def test_verify_long_context_split_plan(tree):
     check(f"long context tree={tree} S={S}", out, ref, lse, rl, bf16_out=bf16)
 
 
+@pytest.mark.parametrize("tree", [False, True])
+def test_verify_tiles_long_context_split_plan(tree):
+    """Wide drafts on the tile kernel (16 and 24 tokens x G = 8: 128 and 192
+    (token, head) pairs per KV head, one and two 128-row tiles) on two long
+    caches: the automatic plan splits each request into chunks (sink in
+    chunk 0 only), the shorter request into fewer, and the finish pass
+    merges them; drafted keys sit at the very end of each cache."""
+    rng = np.random.default_rng(830 + int(tree))
+    ql = [16, 24]
+    b = W.make_batch(rng, kind="prefill", qlens=ql, kv_lens=[65536, 20003], hq=64, hkv=8,
+                     paged=True, sinks="normal")
+    if tree:
+        b.draft_mask = np.concatenate([W.tree_mask(W.draft_tree(rng, n)) for n in ql])
+    from gqa_attention_sinks_attn_amd import sink_attn_verify_num_splits
+    S = sink_attn_verify_num_splits(2, 64, 8, 24, 65536, 0)
+    assert S > 1
+    out, lse, bf16 = run(b, "verify", 0)
+    ref, rl = oracle.attend(b)
+    check(f"tiles long context tree={tree} S={S}", out, ref, lse, rl, bf16_out=bf16)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 5])
+def test_verify_tiles_group16_and_extreme_sinks(splits):
+    """The tile kernel at G = 16 (64 query / 4 KV heads, 8 tokens = 128 rows)
+    with sinks of -1e4 and +10 and a request whose cache is only its draft."""
+    rng = np.random.default_rng(850 + splits)
+    s = rng.standard_normal(64).astype(np.float32)
+    s[[0, 17, 42]] = -1e4
+    s[[5, 31, 63]] = 10.0
+    ql = [8, 8, 5, 8]
+    b = W.make_batch(rng, kind="prefill", qlens=ql, kv_lens=[8, 3000, 777, 1500], hq=64, hkv=4,
+                     paged=True, sinks=s, out_dtype="bf16")
+    out, lse, bf16 = run(b, "verify", splits)
+    ref, rl = oracle.attend(b)
+    check(f"tiles G=16 S={splits}", out, ref, lse, rl, bf16_out=bf16)
+
+
 @pytest.mark.parametrize("qlen,tree", [(4, False), (4, True), (40, True), (33, False)])
 def test_verify_without_lse_bf16(qlen, tree):
     """lse = NULL and bf16 output, on the column-group kernel (4 tokens) and
-    on the prefill tiles the automatic plan picks for wide drafts (33, 40)."""
+    on the tile kernel the plan picks for wide drafts (33, 40)."""
     from gqa_attention_sinks_attn_amd import device
     rng = np.random.default_rng(810 + qlen + int(tree))
     B = 10
