@@ -317,16 +317,23 @@ sink_attn_status sink_attn_decode_balanced_finish(
  *   total_q, max_qlen host scalars: rows, and an upper bound of qlen_b.
  *                    max_qlen must be <= 64 (SINK_ATTN_ERR_UNSUPPORTED
  *                    otherwise: use sink_attn_prefill).  A (request, KV
- *                    head) has C = max_qlen x Hq / Hkv (token, head) pairs;
- *                    each chunk runs one workgroup when C <= 16, else
- *                    ceil(C / 32) workgroups of 32 pairs.  Under the
- *                    automatic plan, C > 128 with Hq / Hkv in {1, 2, 4, 8}
- *                    runs the prefill kernel's 256-row tiles instead (one
- *                    chunk, no workspace).
- *   num_splits       0: automatic plan (sink_attn_verify_num_splits: one
- *                    chunk per request when the grid already holds >= 256
- *                    workgroups, else enough chunks of >= 16 pages for about
- *                    512).  S > 0: S chunks per request, as sink_attn_decode.
+ *                    head) has C = max_qlen x Hq / Hkv (token, head) pairs.
+ *                    C <= 64: each chunk runs one workgroup when C <= 16,
+ *                    else ceil(C / 32) workgroups of 32 pairs.  C > 64 (with
+ *                    Hq / Hkv in {1, 2, 4, 8, 16}): each chunk runs
+ *                    ceil(C / 128) workgroups of 128 pairs that stage the
+ *                    request's K/V tiles in LDS, and chunks are whole
+ *                    64-key tiles.
+ *   num_splits       0: automatic plan (sink_attn_verify_num_splits).  C <=
+ *                    64: one chunk per request when the grid already holds
+ *                    >= 256 workgroups, else enough chunks of >= 16 pages
+ *                    for about 512.  C > 64: one chunk while the (request,
+ *                    KV head, 128-pair group) units reach 512, else chunks
+ *                    of >= 512 keys towards 512 workgroups, at most 64.
+ *                    S > 0: S chunks per request of ceil(max_kv_len / S)
+ *                    keys, rounded up to a multiple of 16 (C <= 64) or of
+ *                    64 (C > 64; at most 64 chunks); a chunk past a
+ *                    request's keys is empty.
  *   out, lse         [total_q, Hq, 64] in out_dtype; fp32 [total_q, Hq] or
  *                    NULL (natural log).
  *   workspace        sink_attn_verify_workspace_size() bytes (0 with one
