@@ -256,7 +256,6 @@ sink_attn_status sink_attn_prefill(const void* q, const int32_t* qo_indptr, cons
   a.out = out;
   a.out_f32 = out_dtype == SINK_ATTN_F32;
   a.lse = lse;
-  a.draft_mask = nullptr;
   return hip_status(sa::launch_prefill(a, num_qo_heads / num_kv_heads,
                                        static_cast<hipStream_t>(stream)),
                     "prefill launch");

@@ -117,7 +117,6 @@ struct PrefillArgs {
   void* out;
   int32_t out_f32;
   float* lse;
-  const uint64_t* draft_mask;   // [total_q] drafted-token visibility (with causal), or nullptr
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);

@@ -122,27 +122,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int s = 0; s < 4; ++s) bq[cb][s] = as_bf16x8(valid[cb] ? ld16(qrow + 16 * s) : z);
   }
 
-  // ---- draft mask (drafted-token verification of a tree): row t sees every
-  // key below pos_base and drafted key pos_base + i when bit i of its word
-  // is set; it replaces causality inside the draft ----
-  const bool tree = p.draft_mask != nullptr;
-  uint32_t mlo[2] = {0u, 0u}, mhi[2] = {0u, 0u};
-  if (tree) {
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      if (valid[cb]) {
-        const uint64_t w = p.draft_mask[q_begin + tok[cb]];
-        mlo[cb] = (uint32_t)w;
-        mhi[cb] = (uint32_t)(w >> 32);
-      }
-    }
-  }
-
   // ---- key range of the workgroup ----
   const int last_tok_wg = min(t0 + T, qlen) - 1;
   const int pos_min_wg = pos_base + t0;
   const int pos_max_wg = pos_base + last_tok_wg;
-  const int kv_hi = (p.causal && !tree) ? min(L, pos_max_wg + 1) : L;
+  const int kv_hi = p.causal ? min(L, pos_max_wg + 1) : L;
   const int n_tiles = (kv_hi + kTile - 1) / kTile;
 
   // ---- online state (log2 units); the sink starts every row ----
@@ -235,13 +219,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     load_tile(kt + 1);   // clamped: the last iteration repeats the last tile
     load_ids(kt + 2);
     const int key0 = kt * kTile;
-    const bool wave_live = !p.causal || tree || key0 <= wave_pos_max;
+    const bool wave_live = !p.causal || key0 <= wave_pos_max;
     if (wave_live) {
       const uint16_t* kbuf = lds_k + buf * kKBuf;
       const uint16_t* vbuf = lds_v + buf * kVBuf;
-      const bool edge = (tree ? key0 + kTile > pos_base
-                              : (p.causal && key0 + kTile - 1 > pos_min_wg)) ||
-                        (key0 + kTile > L);
+      const bool edge = (p.causal && key0 + kTile - 1 > pos_min_wg) || (key0 + kTile > L);
       const f32x16 zero16 = {};
       // K operand (A of S^T) for k-step s, key block kb: keys 32 kb + r,
       // dims 16 s + 8 hh.  V^T operand (A of O^T) for key block kb, half hf,
@@ -257,22 +239,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       f32x16 sacc[2][2];
       uint32_t pk[2][2][2][4];  // [cb][kb][hf][pair]
       auto mask = [&](int cb) {
-        if (tree) {
-          // draft index of the key at constant offset c: base + c; below 0
-          // a prefix key (seen), from qlen on past the cache (not seen)
-          int base = key0 + 4 * hh - pos_base;
-          asm volatile("" : "+v"(base));
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const int jj = base + 32 * kb + 8 * (j >> 2) + (j & 3);
-              const uint32_t w = jj < 32 ? mlo[cb] : mhi[cb];
-              const bool seen = jj < 0 || (jj < qlen && ((w >> (jj & 31)) & 1u));
-              if (!seen) sacc[kb][cb][j] = -INFINITY;
-            }
-          return;
-        }
         const int lim = p.causal ? min(pos[cb], L - 1) : L - 1;
         int rel = lim - key0 - 4 * hh;
         // defined here, so the compares below cannot be hoisted out of the
