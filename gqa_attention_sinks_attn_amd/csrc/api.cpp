@@ -602,14 +602,14 @@ constexpr int32_t kVerifyTileMinColumns = 64;
 constexpr int32_t kVerifyTileRows = 128;
 constexpr int32_t kVerifyTileKeys = 64;
 constexpr int32_t kVerifyTileMaxChunks = 64;
-// Automatic chunking of the tile kernel: one chunk per request while the
-// (request, KV head, row tile) units alone give kVerifyTileTargetWorkgroups
-// workgroups (two per CU); below that, enough chunks of at least 8 tiles
-// (512 keys) to reach it.  Chunks cost partial writes and a merge pass
-// (measured on 64 requests x 16 tokens, L <= 4,096, 512 units: first pass
-// 96 us in one chunk, 79 us in two, plus 24 us of merge), so a grid that
-// already fills the GPU is not split.
-constexpr int64_t kVerifyTileTargetWorkgroups = 512;
+// Automatic chunking of the tile kernel: enough chunks of at least 8 tiles
+// (512 keys) for about kVerifyTileTargetWorkgroups workgroups if every
+// request had max_kv_len keys.  One workgroup per (request, KV head) lets
+// the longest requests bound a ragged batch; chunks cut them at the price of
+// partial writes and a merge pass (measured on 64 requests x 16 tokens, L
+// <= 4,096, 512 units: 96 us in one chunk; 72 + 9 us in two; 77 + 9 us in
+// three).
+constexpr int64_t kVerifyTileTargetWorkgroups = 1024;
 constexpr int32_t kVerifyTileMinChunkTiles = 8;
 
 bool verify_uses_tiles(int32_t group, int32_t columns) {

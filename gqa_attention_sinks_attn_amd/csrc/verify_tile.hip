@@ -378,84 +378,95 @@ void verify_tile_kernel(VerifyTileArgs p) {
   }
 }
 
-// One wave per (request, drafted token, query head), lane = dim: merges the
-// n > 1 chunk partials of a request that spans several chunks by
-// log-sum-exp (L = max lse_c, w_c = e^(lse_c - L), o = sum w_c o_c / sum w_c,
-// lse = L + ln sum w_c).  Requests in one chunk were written by the first
-// pass.  Every lane reads the same log-sum-exps (one transaction each) and
-// its own dim of the partial rows, eight chunks per batch, all loads of a
-// batch in flight together: no cross-lane traffic, one round trip after
-// the request's metadata for up to eight chunks.
+// One workgroup per (request, drafted token).  Wave w merges head groups
+// w, w + 4, ... of four query heads each; lane l takes head 4 grp + l / 16
+// and dims 4 (l % 16) .. + 3 of the group.  Merges the n > 1 chunk
+// partials of a request that spans several chunks by log-sum-exp (L = max
+// lse_c, w_c = e^(lse_c - L), o = sum w_c o_c / sum w_c, lse = L + ln sum
+// w_c); requests in one chunk were written by the first pass.  The
+// log-sum-exps and 16-byte row pieces of four head groups and up to four
+// chunks are loaded in one batch, all in flight together: one round trip
+// after the request's lengths, and no cross-lane traffic.
 __global__ __launch_bounds__(256) void verify_tile_finish_kernel(VerifyTileArgs p) {
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 4;   // chunks per batch of loads
+  constexpr int kGroups = 4;  // head groups per wave and batch
   const int lane = thread_x() & 63;
-  const int64_t idx = (int64_t)block_x() * 4 + __builtin_amdgcn_readfirstlane(thread_x() >> 6);
-  const int64_t per_b = (int64_t)p.max_qlen * p.hq;
-  if (idx >= (int64_t)p.batch * per_b) return;
-  const int b = (int)(idx / per_b);
-  const int t = (int)((idx % per_b) / p.hq);
-  const int h = (int)(idx % p.hq);
+  const int wave = __builtin_amdgcn_readfirstlane(thread_x() >> 6);
+  const int b = block_x() / p.max_qlen;
+  const int t = block_x() % p.max_qlen;
   const int q0 = __builtin_amdgcn_readfirstlane(p.qo_indptr[b]);
   const int qlen = __builtin_amdgcn_readfirstlane(p.qo_indptr[b + 1]) - q0;
   if (t >= qlen) return;
   const int n = n_chunks_of(__builtin_amdgcn_readfirstlane(p.kv_len[b]), p.chunk_tiles);
   if (n <= 1) return;
-  const int64_t pair = (int64_t)(q0 + t) * p.hq + h;
-  const float* ls = p.lse_part + pair * p.max_chunks;
-  const float* os = p.o_part + pair * p.max_chunks * kD + lane;
-
-  // the first batch: log-sum-exps and rows together (indices clamped; the
-  // extra slots repeat chunk n - 1 and weigh nothing)
-  float lv[kBatch], ov[kBatch];
+  const int groups = (p.hq + 3) / 4;
+  const int q4 = lane & 15;
+  for (int g0 = wave; g0 < groups; g0 += 4 * kGroups) {
+    int64_t pair[kGroups];
+    bool live[kGroups];
+    float lv[kGroups][kBatch];
+    f32x4 ov[kGroups][kBatch];
 #pragma unroll
-  for (int j = 0; j < kBatch; ++j) {
-    const int cj = min(j, n - 1);
-    lv[j] = ls[cj];
-    ov[j] = os[(int64_t)cj * kD];
-  }
-  float Lm = -INFINITY;
+    for (int i = 0; i < kGroups; ++i) {
+      const int h = 4 * (g0 + 4 * i) + (lane >> 4);
+      live[i] = g0 + 4 * i < groups && h < p.hq;
+      pair[i] = (int64_t)(q0 + t) * p.hq + (live[i] ? h : 0);
 #pragma unroll
-  for (int j = 0; j < kBatch; ++j) Lm = fmaxf(Lm, lv[j]);
-  for (int c0 = kBatch; c0 < n; c0 += kBatch) {
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) Lm = fmaxf(Lm, ls[min(c0 + j, n - 1)]);
-  }
-  auto weight = [&](float lc) {
-    if (Lm == -INFINITY) return 0.f;
-    if (Lm == INFINITY) return lc == INFINITY ? 1.f : 0.f;
-    return __expf(lc - Lm);
-  };
-  float den = 0.f, acc = 0.f;
-#pragma unroll
-  for (int j = 0; j < kBatch; ++j) {
-    const float w = j < n ? weight(lv[j]) : 0.f;
-    den += w;
-    acc += w != 0.f ? w * ov[j] : 0.f;
-  }
-  for (int c0 = kBatch; c0 < n; c0 += kBatch) {
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int cj = min(c0 + j, n - 1);
-      lv[j] = ls[cj];
-      ov[j] = os[(int64_t)cj * kD];
+      for (int j = 0; j < kBatch; ++j) {
+        const int64_t slot = pair[i] * p.max_chunks + min(j, n - 1);
+        lv[i][j] = p.lse_part[slot];
+        ov[i][j] = *reinterpret_cast<const f32x4*>(p.o_part + slot * kD + 4 * q4);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const float w = c0 + j < n ? weight(lv[j]) : 0.f;
-      den += w;
-      acc += w != 0.f ? w * ov[j] : 0.f;
+    for (int i = 0; i < kGroups; ++i) {
+      if (!live[i]) continue;
+      const float* ls = p.lse_part + pair[i] * p.max_chunks;
+      const float* os = p.o_part + pair[i] * p.max_chunks * kD + 4 * q4;
+      float Lm = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) Lm = fmaxf(Lm, lv[i][j]);
+      for (int c0 = kBatch; c0 < n; c0 += kBatch)
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) Lm = fmaxf(Lm, ls[min(c0 + j, n - 1)]);
+      auto weight = [&](float lc) {
+        if (Lm == -INFINITY) return 0.f;
+        if (Lm == INFINITY) return lc == INFINITY ? 1.f : 0.f;
+        return __expf(lc - Lm);
+      };
+      float den = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const float w = j < n ? weight(lv[i][j]) : 0.f;
+        den += w;
+        if (w != 0.f) acc += w * ov[i][j];
+      }
+      for (int c0 = kBatch; c0 < n; c0 += kBatch) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int cj = min(c0 + j, n - 1);
+          const float w = c0 + j < n ? weight(ls[cj]) : 0.f;
+          den += w;
+          if (w != 0.f) acc += w * *reinterpret_cast<const f32x4*>(os + (int64_t)cj * kD);
+        }
+      }
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+      const int64_t dst = pair[i] * kD + 4 * q4;
+      if (p.out_f32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + dst) = acc * inv;
+      } else {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + dst) =
+            u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+      }
+      if (p.lse != nullptr && q4 == 0) {
+        float l;
+        if (Lm == -INFINITY) l = -INFINITY;
+        else if (Lm == INFINITY) l = INFINITY;
+        else l = Lm + __logf(den);
+        p.lse[pair[i]] = l;
+      }
     }
-  }
-  const float o = den > 0.f ? acc / den : 0.f;
-  const int64_t dst = pair * kD + lane;
-  if (p.out_f32) reinterpret_cast<float*>(p.out)[dst] = o;
-  else reinterpret_cast<uint16_t*>(p.out)[dst] = float_to_bf16_bits(o);
-  if (p.lse != nullptr && lane == 0) {
-    float l;
-    if (Lm == -INFINITY) l = -INFINITY;
-    else if (Lm == INFINITY) l = INFINITY;
-    else l = Lm + __logf(den);
-    p.lse[pair] = l;
   }
 }
 
@@ -471,10 +482,10 @@ hipError_t launch_g(const VerifyTileArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((verify_tile_kernel<G, false>), dim3((unsigned)wgs), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_chunks == 1) return e;
-  const int64_t waves = (int64_t)a.batch * a.max_qlen * a.hq;
-  if (waves == 0) return hipSuccess;
-  hipLaunchKernelGGL(verify_tile_finish_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
-                     stream, a);
+  const int64_t rows = (int64_t)a.batch * a.max_qlen;   // (request, token) slots
+  if (rows == 0) return hipSuccess;
+  if (rows > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(verify_tile_finish_kernel, dim3((unsigned)rows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

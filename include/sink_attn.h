@@ -327,9 +327,9 @@ sink_attn_status sink_attn_decode_balanced_finish(
  *   num_splits       0: automatic plan (sink_attn_verify_num_splits).  C <=
  *                    64: one chunk per request when the grid already holds
  *                    >= 256 workgroups, else enough chunks of >= 16 pages
- *                    for about 512.  C > 64: one chunk while the (request,
- *                    KV head, 128-pair group) units reach 512, else chunks
- *                    of >= 512 keys towards 512 workgroups, at most 64.
+ *                    for about 512.  C > 64: chunks of >= 512 keys towards
+ *                    1,024 workgroups of (request, KV head, 128-pair
+ *                    group, chunk), at most 64 chunks.
  *                    S > 0: S chunks per request of ceil(max_kv_len / S)
  *                    keys, rounded up to a multiple of 16 (C <= 64) or of
  *                    64 (C > 64; at most 64 chunks); a chunk past a
