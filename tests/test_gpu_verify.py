@@ -214,6 +214,28 @@ def test_verify_tiles_group16_and_extreme_sinks(splits):
     check(f"tiles G=16 S={splits}", out, ref, lse, rl, bf16_out=bf16)
 
 
+@pytest.mark.parametrize("tree", [False, True])
+@pytest.mark.parametrize("hq,hkv,qlens", [(32, 16, [64, 40, 33]),       # G = 2: 1 row tile
+                                          (64, 4, [64, 17, 9]),         # G = 16: up to 8 row tiles
+                                          (64, 8, [64, 1, 30, 16])])    # G = 8: 4 row tiles, a 1-token row
+@pytest.mark.parametrize("splits", [0, 3])
+def test_verify_tiles_row_tiles_and_group_sizes(hq, hkv, qlens, tree, splits):
+    """The tile kernel at group sizes 2, 8 and 16 with drafts up to the
+    64-token maximum (several 128-row tiles per (request, KV head), the last
+    one partly padding), mixed draft lengths in one batch, causal and tree
+    masks, one or three chunks."""
+    rng = np.random.default_rng(870 + hq + hkv + int(tree) + splits)
+    L = [int(n) + int(rng.integers(0, 1500)) for n in qlens]
+    if tree:
+        b = _tree_batch(int(rng.integers(1 << 30)), qlens, L, hq, hkv)
+    else:
+        b = W.make_batch(rng, kind="prefill", qlens=qlens, kv_lens=L, hq=hq, hkv=hkv, paged=True,
+                         sinks="normal")
+    out, lse, bf16 = run(b, "verify", splits)
+    ref, rl = oracle.attend(b)
+    check(f"tiles G={hq // hkv} tree={tree} S={splits}", out, ref, lse, rl, bf16_out=bf16)
+
+
 @pytest.mark.parametrize("qlen,tree", [(4, False), (4, True), (40, True), (33, False)])
 def test_verify_without_lse_bf16(qlen, tree):
     """lse = NULL and bf16 output, on the column-group kernel (4 tokens) and
