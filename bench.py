@@ -55,7 +55,7 @@ EVENT_EVERY = 4                # timed decode steps between two sampled first-pa
 # 256 MiB copy; see profiles/.  Valid for the kernel sources they were taken
 # on -- reset to None whenever decode_balanced.hip or prefill.hip changes.
 DECODE_TRAFFIC_BYTES = 260_940_849
-PREFILL_TRAFFIC_BYTES = 1_879_642_360
+PREFILL_TRAFFIC_BYTES = None
 
 
 def log(msg: str):

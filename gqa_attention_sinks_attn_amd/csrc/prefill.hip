@@ -51,17 +51,6 @@ constexpr int kKBuf = kTile * kKPitch;
 constexpr int kVBuf = kTile * kVPitch;
 constexpr float kFastLimit = 32768.f; // lane-partial tile sum that forces a rescale
 
-template <bool PAGED>
-__device__ __forceinline__ const uint16_t* kv_row(const PrefillArgs& p, const uint16_t* base,
-                                                  int g, int key, int kv_start) {
-  if constexpr (PAGED) {
-    const int page = p.page_indices[kv_start + (key >> 4)];
-    return base + (((int64_t)page * p.hkv + g) * 16 + (key & 15)) * kD;
-  } else {
-    return base + ((int64_t)(kv_start + key) * p.hkv + g) * kD;
-  }
-}
-
 // acc + lo(w) + hi(w) for a packed bf16 pair, accumulated in fp32.
 __device__ __forceinline__ float dot2_sum(uint32_t w, float acc) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -152,11 +141,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int ld_chunk = tid & 7;  // 16-byte chunk within a 128-byte row
   u32x4 rk0, rk1, rv0, rv1;
   // Loads are unconditional (no branch, so the compiler's waits stay
-  // exact): tiles past the last one are clamped to it, and rows past the
-  // last key read row 0 of the request.  Their scores are masked (every tile
-  // holding such rows is an edge tile), and their V rows are zeroed when
-  // stored (their weight is 0, and 0 x garbage must stay 0).
-  const int64_t vdelta = p.v - p.k;
+  // exact): tiles past the last one are clamped to it, and a row past the
+  // last key reads key 0 (contiguous) or the same slot of the request's
+  // first page (paged).  Their scores are masked (every tile holding such
+  // rows is an edge tile), and their V rows are zeroed when stored (their
+  // weight is 0, and 0 x garbage must stay 0).  A row's address is one
+  // unsigned multiply-add: key x row stride (contiguous), or page id x page
+  // stride (paged: tiles start on page boundaries, so a thread's offset
+  // inside a page is fixed).
+  const int64_t vdelta = reinterpret_cast<const char*>(p.v) - reinterpret_cast<const char*>(p.k);
+  const uint32_t stride_bytes = PAGED ? (uint32_t)p.hkv * 16 * kD * 2   // one page
+                                      : (uint32_t)p.hkv * kD * 2;       // one key
+  const char* kbase =
+      reinterpret_cast<const char*>(p.k) + 16 * ld_chunk +
+      (PAGED ? (int64_t)g * 16 * kD * 2 + (ld_row & 15) * kD * 2
+             : ((int64_t)kv_start * p.hkv + g) * kD * 2);
   auto tile_key0 = [&](int kt) { return min(kt, n_tiles - 1) * kTile; };
   // Paged caches: the page ids of this thread's two rows are loaded one
   // tile before the rows themselves, so a tile's K/V loads do not wait for
@@ -164,25 +163,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int id_a = 0, id_b = 0;
   auto load_ids = [&](int kt) {
     if constexpr (PAGED) {
+      const int32_t* pages = p.page_indices + kv_start;
       const int key0 = tile_key0(kt);
-      const int ka = key0 + ld_row, kb2 = key0 + 32 + ld_row;
-      id_a = p.page_indices[kv_start + ((ka < L ? ka : 0) >> 4)];
-      id_b = p.page_indices[kv_start + ((kb2 < L ? kb2 : 0) >> 4)];
-    }
-  };
-  auto row_ptr = [&](int key, int id) -> const uint16_t* {
-    if constexpr (PAGED) {
-      return p.k + (((int64_t)id * p.hkv + g) * 16 + (key & 15)) * kD;
-    } else {
-      (void)id;
-      return kv_row<PAGED>(p, p.k, g, key, kv_start);
+      const int pg = (key0 >> 4) + (ld_row >> 4);
+      id_a = pages[key0 + ld_row < L ? pg : 0];
+      id_b = pages[key0 + 32 + ld_row < L ? pg + 2 : 0];
     }
   };
   auto load_tile = [&](int kt) {
-    const int key0 = tile_key0(kt);
-    const int ka = key0 + ld_row, kb2 = key0 + 32 + ld_row;
-    const uint16_t* pa = row_ptr(ka < L ? ka : 0, id_a) + 8 * ld_chunk;
-    const uint16_t* pb = row_ptr(kb2 < L ? kb2 : 0, id_b) + 8 * ld_chunk;
+    uint32_t ua, ub;
+    if constexpr (PAGED) {
+      (void)kt;
+      ua = (uint32_t)id_a;
+      ub = (uint32_t)id_b;
+    } else {
+      const int key0 = tile_key0(kt);
+      const int ka = key0 + ld_row, kb2 = key0 + 32 + ld_row;
+      ua = (uint32_t)(ka < L ? ka : 0);
+      ub = (uint32_t)(kb2 < L ? kb2 : 0);
+    }
+    const char* pa = kbase + (uint64_t)ua * stride_bytes;
+    const char* pb = kbase + (uint64_t)ub * stride_bytes;
     rk0 = ld16(pa);
     rk1 = ld16(pb);
     rv0 = ld16(pa + vdelta);

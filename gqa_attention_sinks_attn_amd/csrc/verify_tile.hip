@@ -139,29 +139,30 @@ void verify_tile_kernel(VerifyTileArgs p) {
 
   // ---- tile loader: thread -> rows ld_row and 32 + ld_row, one 16 B chunk.
   // Loads are unconditional: tiles past the chunk repeat its last tile, and
-  // rows past the last key read key 0 (their V rows are zeroed when stored,
-  // their scores masked: every tile holding them is an edge tile). ----
+  // a row past the last key reads the same slot of the request's first page
+  // (its V row is zeroed when stored, its scores masked: every tile holding
+  // such rows is an edge tile).  Tiles start on page boundaries, so a
+  // thread's offset inside a page is fixed and a row's address is one
+  // unsigned multiply-add of its page id. ----
   const int ld_row = tid >> 3;
   const int ld_chunk = tid & 7;
-  const int64_t head_stride = (int64_t)16 * kD;
-  const int64_t page_stride = (int64_t)p.hkv * head_stride;
-  const int64_t vdelta = p.v - p.k;
+  const uint32_t page_bytes = (uint32_t)p.hkv * 16 * kD * 2;   // one page, every KV head
+  const char* kbase = reinterpret_cast<const char*>(p.k) + (int64_t)g * 16 * kD * 2 +
+                      (ld_row & 15) * kD * 2 + 16 * ld_chunk;
+  const int64_t vdelta = reinterpret_cast<const char*>(p.v) - reinterpret_cast<const char*>(p.k);
+  const int32_t* pages = p.page_indices + kv_start;
   u32x4 rk0, rk1, rv0, rv1;
   int id_a = 0, id_b = 0;
   auto tile_key0 = [&](int kt) { return (tile0 + min(kt, n_tiles - 1)) * kTile; };
   auto load_ids = [&](int kt) {
     const int key0 = tile_key0(kt);
-    const int ka = key0 + ld_row, kb2 = key0 + 32 + ld_row;
-    id_a = p.page_indices[kv_start + ((ka < L ? ka : 0) >> 4)];
-    id_b = p.page_indices[kv_start + ((kb2 < L ? kb2 : 0) >> 4)];
+    const int pg = (key0 >> 4) + (ld_row >> 4);
+    id_a = pages[key0 + ld_row < L ? pg : 0];
+    id_b = pages[key0 + 32 + ld_row < L ? pg + 2 : 0];
   };
-  auto load_tile = [&](int kt) {
-    const int key0 = tile_key0(kt);
-    const int ka = key0 + ld_row, kb2 = key0 + 32 + ld_row;
-    const uint16_t* pa = p.k + id_a * page_stride + g * head_stride +
-                         ((ka < L ? ka : 0) & 15) * kD + 8 * ld_chunk;
-    const uint16_t* pb = p.k + id_b * page_stride + g * head_stride +
-                         ((kb2 < L ? kb2 : 0) & 15) * kD + 8 * ld_chunk;
+  auto load_tile = [&]() {
+    const char* pa = kbase + (uint64_t)(uint32_t)id_a * page_bytes;
+    const char* pb = kbase + (uint64_t)(uint32_t)id_b * page_bytes;
     rk0 = ld16(pa);
     rk1 = ld16(pb);
     rv0 = ld16(pa + vdelta);
@@ -169,18 +170,23 @@ void verify_tile_kernel(VerifyTileArgs p) {
   };
   auto store_tile = [&](int buf, int kt) {
     const int key0 = tile_key0(kt);
-    const u32x4 z = {0u, 0u, 0u, 0u};
     uint16_t* kd = lds_k + buf * kKBuf;
     uint16_t* vd = lds_v + buf * kVBuf;
     *reinterpret_cast<u32x4*>(kd + ld_row * kKPitch + 8 * ld_chunk) = rk0;
     *reinterpret_cast<u32x4*>(kd + (32 + ld_row) * kKPitch + 8 * ld_chunk) = rk1;
-    *reinterpret_cast<u32x4*>(vd + ld_row * kVPitch + 8 * ld_chunk) = key0 + ld_row < L ? rv0 : z;
-    *reinterpret_cast<u32x4*>(vd + (32 + ld_row) * kVPitch + 8 * ld_chunk) =
-        key0 + 32 + ld_row < L ? rv1 : z;
+    if (key0 + kTile <= L) {   // wave-uniform: only the last tile has rows past L
+      *reinterpret_cast<u32x4*>(vd + ld_row * kVPitch + 8 * ld_chunk) = rv0;
+      *reinterpret_cast<u32x4*>(vd + (32 + ld_row) * kVPitch + 8 * ld_chunk) = rv1;
+    } else {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(vd + ld_row * kVPitch + 8 * ld_chunk) = key0 + ld_row < L ? rv0 : z;
+      *reinterpret_cast<u32x4*>(vd + (32 + ld_row) * kVPitch + 8 * ld_chunk) =
+          key0 + 32 + ld_row < L ? rv1 : z;
+    }
   };
 
   load_ids(0);
-  load_tile(0);
+  load_tile();
   load_ids(1);
   store_tile(0, 0);
   __syncthreads();
@@ -193,7 +199,7 @@ void verify_tile_kernel(VerifyTileArgs p) {
 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int buf = kt & 1;
-    load_tile(kt + 1);   // clamped: the last iteration repeats the last tile
+    load_tile();         // tile kt + 1 (clamped: the last iteration repeats the last tile)
     load_ids(kt + 2);
     const int key0 = (tile0 + kt) * kTile;
     const uint16_t* kbuf = lds_k + buf * kKBuf;
