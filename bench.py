@@ -54,8 +54,8 @@ EVENT_EVERY = 4                # timed decode steps between two sampled first-pa
 # (python bench.py --mode traffic), each scaled by the same counter on a
 # 256 MiB copy; see profiles/.  Valid for the kernel sources they were taken
 # on -- reset to None whenever decode_balanced.hip or prefill.hip changes.
-DECODE_TRAFFIC_BYTES = 260_940_849
-PREFILL_TRAFFIC_BYTES = None
+DECODE_TRAFFIC_BYTES = 260_946_607
+PREFILL_TRAFFIC_BYTES = 1_882_476_635
 
 
 def log(msg: str):
