@@ -19,8 +19,9 @@
 // plus drafted key P + i when bit i of its word is set.
 //
 // Chunk c covers the 64-key tiles c Ct .. c Ct + Ct - 1 of the request.  The
-// workgroup stages each tile's K and V in LDS once (double-buffered, the
-// next tile's page ids and rows in flight), and every wave computes on it:
+// workgroup loads each tile's K and V straight into LDS (three buffers, the
+// next two tiles in flight while one is computed), and every wave computes
+// on it:
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 for the tile's two 32-key
 //     halves, so a lane holds 16 scores of one row per half;
 //   * the halves are interleaved: the scores of half 1 are computed while
@@ -44,16 +45,53 @@ namespace {
 constexpr int kD = 64;
 constexpr int kTile = 64;             // keys per tile
 constexpr int kRows = 128;            // rows per workgroup (4 waves x 32)
-constexpr int kKPitch = 72;           // K tile row pitch in bf16 (144 B)
-constexpr int kVPitch = 80;           // V tile row pitch in bf16 (160 B)
-constexpr int kKBuf = kTile * kKPitch;
-constexpr int kVBuf = kTile * kVPitch;
+constexpr int kTileBytes = kTile * kD * 2;  // one K or V tile in LDS, rows unpadded
+constexpr int kBufs = 3;                    // LDS tile buffers
 constexpr float kFastLimit = 32768.f; // lane-partial half-tile sum that forces a rescale
 
 // acc + lo(w) + hi(w) for a packed bf16 pair, accumulated in fp32.
 __device__ __forceinline__ float dot2_sum(uint32_t w, float acc) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
+// Wait until at most N vector memory operations of this wave are
+// outstanding (the LDS-direct tile loads count among them).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// 16 bytes per lane from global memory into LDS: lane l reads base + off
+// and writes LDS bytes lds + 16 l .. lds + 16 l + 15 (base and lds
+// wave-uniform).  Written as assembly so that the compiler neither counts
+// nor waits for these loads: wait_vmem and the workgroup barrier order
+// them against the LDS reads.
+// M0 carries the LDS address; the compiler keeps no value of its own in it
+// (the clobber is declared, the warning about it silenced).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS offset of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding global load); the empty assembly statements
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ int n_chunks_of(int L, int chunk_tiles) {
@@ -64,8 +102,8 @@ __device__ __forceinline__ int n_chunks_of(int L, int chunk_tiles) {
 template <int G, bool TREE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void verify_tile_kernel(VerifyTileArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * kKBuf];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * kVBuf];
+  __shared__ __attribute__((aligned(1024))) char lds_k[kBufs * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v[kBufs * kTileBytes];
 
   // flat index -> (work item = c * B * Hkv + unit, row tile rt): the row
   // tiles of one item go to the same XCD (workgroups are dealt to the 8 XCDs
@@ -137,73 +175,112 @@ void verify_tile_kernel(VerifyTileArgs p) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
 
-  // ---- tile loader: thread -> rows ld_row and 32 + ld_row, one 16 B chunk.
-  // Loads are unconditional: tiles past the chunk repeat its last tile, and
-  // a row past the last key reads the same slot of the request's first page
-  // (its V row is zeroed when stored, its scores masked: every tile holding
-  // such rows is an edge tile).  Tiles start on page boundaries, so a
-  // thread's offset inside a page is fixed and a row's address is one
-  // unsigned multiply-add of its page id. ----
-  const int ld_row = tid >> 3;
-  const int ld_chunk = tid & 7;
+  // ---- tile loader.  A tile's K and V go straight from global memory
+  // into LDS, 1 KiB blocks of eight key rows (key row r in block r / 8).
+  // Wave w loads page w of every tile: K and V rows 16 w .. 16 w + 15, two
+  // blocks each, one page id (wave-uniform, a scalar load) and a fixed
+  // offset per lane inside the page.  The lane -> (row, 16-byte chunk) map
+  // of a block lays it out as the operand reads want it (chunk c of row
+  // r' = r % 8, e = (r / 8) % 2):
+  //   K: slot 16 (c / 2) + ((2 r' + c % 2 + e) mod 16), so the 16 rows of
+  //      one K-operand read fall in 16 different bank groups and k-step s
+  //      is a constant offset;
+  //   V: slot 16 (c / 4 + 2 (r' / 4)) + 4 (r' % 4) + c % 4, so the four
+  //      rows x four chunks of one transposed read fall in 16 different
+  //      bank groups and every V^T operand is a constant offset.
+  // Rows past the last key read key 0 (a key of the request, so finite):
+  // their scores are masked, so P is 0 for them. ----
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t page_bytes = (uint32_t)p.hkv * 16 * kD * 2;   // one page, every KV head
-  const char* kbase = reinterpret_cast<const char*>(p.k) + (int64_t)g * 16 * kD * 2 +
-                      (ld_row & 15) * kD * 2 + 16 * ld_chunk;
-  const int64_t vdelta = reinterpret_cast<const char*>(p.v) - reinterpret_cast<const char*>(p.k);
+  const char* kbytes = reinterpret_cast<const char*>(p.k);
+  const char* vbytes = reinterpret_cast<const char*>(p.v);
   const int32_t* pages = p.page_indices + kv_start;
-  u32x4 rk0, rk1, rv0, rv1;
-  int id_a = 0, id_b = 0;
-  auto tile_key0 = [&](int kt) { return (tile0 + min(kt, n_tiles - 1)) * kTile; };
-  auto load_ids = [&](int kt) {
-    const int key0 = tile_key0(kt);
-    const int pg = (key0 >> 4) + (ld_row >> 4);
-    id_a = pages[key0 + ld_row < L ? pg : 0];
-    id_b = pages[key0 + 32 + ld_row < L ? pg + 2 : 0];
+  uint32_t koff[2], voff[2], kzero[2], vzero[2];
+  int krow[2], vrow[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int x = ((lane & 15) - e) & 15;
+    const int kc = 2 * (lane >> 4) + (x & 1);
+    krow[e] = 8 * e + (x >> 1);
+    koff[e] = (uint32_t)g * 16 * kD * 2 + krow[e] * kD * 2 + 16 * kc;
+    kzero[e] = (uint32_t)g * 16 * kD * 2 + 16 * kc;
+    const int vc = 4 * ((lane >> 4) & 1) + (lane & 3);
+    vrow[e] = 8 * e + 4 * (lane >> 5) + ((lane & 15) >> 2);
+    voff[e] = (uint32_t)g * 16 * kD * 2 + vrow[e] * kD * 2 + 16 * vc;
+    vzero[e] = (uint32_t)g * 16 * kD * 2 + 16 * vc;
+  }
+  auto tile_key0 = [&](int kt) { return (tile0 + kt) * kTile; };
+  // Page ids of this wave's page in tiles first .. first + 63, one per lane,
+  // loaded together and read out with v_readlane (a wave-uniform value);
+  // the assembly use makes the compiler wait for them right here.
+  auto load_ids = [&](int first) {
+    const int kt = first + lane;
+    int id = 0;
+    if (kt < n_tiles) {
+      const int key0 = tile_key0(kt);
+      id = pages[key0 + 16 * wave_u < L ? (key0 >> 4) + wave_u : 0];
+    }
+    asm volatile("" ::"v"(id));
+    return id;
   };
-  auto load_tile = [&]() {
-    const char* pa = kbase + (uint64_t)(uint32_t)id_a * page_bytes;
-    const char* pb = kbase + (uint64_t)(uint32_t)id_b * page_bytes;
-    rk0 = ld16(pa);
-    rk1 = ld16(pb);
-    rv0 = ld16(pa + vdelta);
-    rv1 = ld16(pb + vdelta);
-  };
-  auto store_tile = [&](int buf, int kt) {
+  auto issue = [&](int kt, int bf, int id) {
     const int key0 = tile_key0(kt);
-    uint16_t* kd = lds_k + buf * kKBuf;
-    uint16_t* vd = lds_v + buf * kVBuf;
-    *reinterpret_cast<u32x4*>(kd + ld_row * kKPitch + 8 * ld_chunk) = rk0;
-    *reinterpret_cast<u32x4*>(kd + (32 + ld_row) * kKPitch + 8 * ld_chunk) = rk1;
-    if (key0 + kTile <= L) {   // wave-uniform: only the last tile has rows past L
-      *reinterpret_cast<u32x4*>(vd + ld_row * kVPitch + 8 * ld_chunk) = rv0;
-      *reinterpret_cast<u32x4*>(vd + (32 + ld_row) * kVPitch + 8 * ld_chunk) = rv1;
-    } else {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(vd + ld_row * kVPitch + 8 * ld_chunk) = key0 + ld_row < L ? rv0 : z;
-      *reinterpret_cast<u32x4*>(vd + (32 + ld_row) * kVPitch + 8 * ld_chunk) =
-          key0 + 32 + ld_row < L ? rv1 : z;
+    const char* kp = kbytes + (uint64_t)(uint32_t)id * page_bytes;
+    const char* vp = vbytes + (uint64_t)(uint32_t)id * page_bytes;
+    const uint32_t kd = lds_offset(lds_k) + bf * kTileBytes + wave_u * 2048;
+    const uint32_t vd = lds_offset(lds_v) + bf * kTileBytes + wave_u * 2048;
+    const bool tail = key0 + kTile > L;   // wave-uniform: only the last tile
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      uint32_t ko = koff[e], vo = voff[e];
+      if (tail) {
+        const int row0 = key0 + 16 * wave_u;
+        ko = row0 + krow[e] < L ? ko : kzero[e];
+        vo = row0 + vrow[e] < L ? vo : vzero[e];
+      }
+      load_lds16(kp, ko, kd + 1024 * e);
+      load_lds16(vp, vo, vd + 1024 * e);
     }
   };
 
-  load_ids(0);
-  load_tile();
-  load_ids(1);
-  store_tile(0, 0);
-  __syncthreads();
+  // the prologue's own global loads complete here, not inside the loop
+  asm volatile("" ::"v"(bq[0]), "v"(bq[1]), "v"(bq[2]), "v"(bq[3]));
+  int ids = load_ids(0);
+  issue(0, 0, __builtin_amdgcn_readlane(ids, 0));
+  if (n_tiles > 1) issue(1, 1, __builtin_amdgcn_readlane(ids, 1));
 
   const float sl2 = p.scale_log2;
-  // transposed V reads: 16-lane group q = lane / 16 covers dims 16 (q % 2) ..
-  // of a 32-dim block and keys 4 hh + s / 4 (s = lane % 16)
-  const int tr_row = 4 * hh + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // Operand reads, byte offsets inside a tile buffer.  K operand of k-step
+  // s, half kb: key 32 kb + r, dims 16 s + 8 hh (chunk 2 s + hh) at
+  // kread + 4096 kb + 256 s.  V^T operand: the transposed read of 16-lane
+  // group q = lane / 16 covers dims 16 (q % 2) + 4 (lane % 4) .. of a 32-dim
+  // block db (chunk 2 (q % 2) + (lane % 4) / 2 + 4 db) and key row
+  // 4 hh + (lane % 16) / 4 (+ 8 for the upper four values) of the 16-key
+  // slice hf of half kb, at vread + 4096 kb + 2048 hf + 256 db (+ 1024).
+  const int kread = ((lane & 31) >> 3) * 1024 + 16 * ((2 * (lane & 7) + hh + ((lane >> 3) & 1)) & 15);
+  const int vread = 512 * hh + 64 * ((lane & 15) >> 2) + 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) +
+                    8 * (lane & 1);
 
   for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
-    load_tile();         // tile kt + 1 (clamped: the last iteration repeats the last tile)
-    load_ids(kt + 2);
+    const int buf = kt % kBufs;
+    // this wave's part of tile kt has landed (tile kt + 1 may be in
+    // flight); the barrier makes every part visible and frees the buffer of
+    // tile kt - 1 for tile kt + 2
+    if (kt + 1 < n_tiles) wait_vmem<4>();
+    else wait_vmem<0>();
+    barrier_only();
+    if (kt + 2 < n_tiles) {
+      if (((kt + 2) & 63) == 0) ids = load_ids(kt + 2);
+      issue(kt + 2, (kt + 2) % kBufs, __builtin_amdgcn_readlane(ids, (kt + 2) & 63));
+    }
     const int key0 = (tile0 + kt) * kTile;
-    const uint16_t* kbuf = lds_k + buf * kKBuf;
-    const uint16_t* vbuf = lds_v + buf * kVBuf;
+    const char* kbuf = lds_k + buf * kTileBytes;
+    // V^T reads from one LDS address per tile, hidden from loop strength
+    // reduction, so that each read's constant part becomes its offset
+    uint32_t vaddr = lds_offset(lds_v) + buf * kTileBytes + vread;
+    asm volatile("" : "+v"(vaddr));
+    const __attribute__((address_space(3))) char* vbuf =
+        (const __attribute__((address_space(3))) char*)(uintptr_t)vaddr;
     // tiles that reach the drafted keys (from P) or the end of the cache
     const bool edge = key0 + kTile > P;
     const f32x16 zero16 = {};
@@ -212,11 +289,14 @@ void verify_tile_kernel(VerifyTileArgs p) {
     // 16 s + 8 hh.  V^T operand (A of O^T) for half kb, k-step hf, dim
     // block db: dims 32 db + .., keys 32 kb + 16 hf + {4 hh .., 8 + 4 hh ..}.
     auto kop = [&](int s, int kb) {
-      return as_bf16x8(*reinterpret_cast<const u32x4*>(kbuf + (32 * kb + r) * kKPitch + 16 * s + 8 * hh));
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(kbuf + kread + 4096 * kb + 256 * s));
     };
     auto vop = [&](int kb, int hf, int db) {
-      const uint16_t* src = vbuf + (32 * kb + 16 * hf + tr_row) * kVPitch + tr_col + 32 * db;
-      return as_bf16x8(lds_tr16_pair(src, src + 8 * kVPitch));
+      const auto* src = vbuf + 4096 * kb + 2048 * hf + 256 * db;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 1024));
+      const u32x2 a = __builtin_bit_cast(u32x2, lo), b2 = __builtin_bit_cast(u32x2, hi);
+      return as_bf16x8(u32x4{a[0], a[1], b2[0], b2[1]});
     };
     // S^T[kb]: keys 32 kb + 8 (j / 4) + 4 hh + j % 4, column = this row
     f32x16 sacc[2];
@@ -340,8 +420,6 @@ void verify_tile_kernel(VerifyTileArgs p) {
       const int hf = i >> 1, db = i & 1;
       o[db] = mfma32(vo[1][hf][db], pb_of(1, hf), o[db]);
     }
-    store_tile(buf ^ 1, kt + 1);
-    __syncthreads();
   }
 
   // ---- epilogue: o = O / d, lse = m + log2 d (natural log at the boundary) ----
