@@ -12,8 +12,9 @@
 //     workgroup, so a workgroup covers 256 / G tokens x G heads and every
 //     K/V tile it stages in LDS is reused by all 256 rows (GQA packing);
 //   * keys are walked in tiles of 64 up to the causal edge of the
-//     workgroup's last token; K and V tiles are double-buffered in LDS and
-//     the next tile's global loads are in flight while this one computes;
+//     workgroup's last token; K and V tiles go straight from global memory
+//     into LDS (three buffers: the next two tiles are in flight while one
+//     is computed), laid out for conflict-free operand reads;
 //   * each wave computes S^T = K Q^T for its 2 x 32 rows on
 //     v_mfma_f32_32x32x16_bf16, so a lane holds 32 scores of one query row
 //     and the row maximum needs one cross-lane exchange;
@@ -45,10 +46,8 @@ namespace {
 
 constexpr int kD = 64;
 constexpr int kTile = 64;            // keys per tile
-constexpr int kKPitch = 72;          // K tile row pitch in bf16 (144 B)
-constexpr int kVPitch = 80;          // V tile row pitch in bf16 (160 B)
-constexpr int kKBuf = kTile * kKPitch;
-constexpr int kVBuf = kTile * kVPitch;
+constexpr int kTileBytes = kTile * kD * 2;  // one K or V tile in LDS, rows unpadded
+constexpr int kBufs = 3;                    // LDS tile buffers
 constexpr float kFastLimit = 32768.f; // lane-partial tile sum that forces a rescale
 
 // acc + lo(w) + hi(w) for a packed bf16 pair, accumulated in fp32.
@@ -60,8 +59,8 @@ __device__ __forceinline__ float dot2_sum(uint32_t w, float acc) {
 template <int G, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs p) {
   constexpr int T = 256 / G;  // tokens per workgroup
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * kKBuf];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * kVBuf];
+  __shared__ __attribute__((aligned(1024))) char lds_k[kBufs * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v[kBufs * kTileBytes];
 
   // Heaviest first: the grid is flat with the round j as its slowest index,
   // and round j takes the j-th query tile from the end of every request.  A
@@ -136,105 +135,150 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int j = 0; j < 16; ++j) o[cb][db][j] = 0.f;
   }
 
-  // ---- tile loader: thread -> rows ld_row and 32 + ld_row, one 16 B chunk ----
-  const int ld_row = tid >> 3;   // 0..31
-  const int ld_chunk = tid & 7;  // 16-byte chunk within a 128-byte row
-  u32x4 rk0, rk1, rv0, rv1;
-  // Loads are unconditional (no branch, so the compiler's waits stay
-  // exact): tiles past the last one are clamped to it, and a row past the
-  // last key reads key 0 (contiguous) or the same slot of the request's
-  // first page (paged).  Their scores are masked (every tile holding such
-  // rows is an edge tile), and their V rows are zeroed when stored (their
-  // weight is 0, and 0 x garbage must stay 0).  A row's address is one
-  // unsigned multiply-add: key x row stride (contiguous), or page id x page
-  // stride (paged: tiles start on page boundaries, so a thread's offset
-  // inside a page is fixed).
-  const int64_t vdelta = reinterpret_cast<const char*>(p.v) - reinterpret_cast<const char*>(p.k);
+  // ---- tile loader.  A tile's K and V go straight from global memory
+  // into LDS (load_lds16), 1 KiB blocks of eight key rows (key row r in
+  // block r / 8).  Wave w loads K and V rows 16 w .. 16 w + 15 of every
+  // tile, two blocks each: on a paged cache one page (one wave-uniform page
+  // id, read with v_readlane from a vector of 64 tiles' ids loaded at
+  // once), on a contiguous one from a wave-uniform row base; each lane's
+  // offset from that base is fixed.  The lane -> (row, 16-byte chunk) map
+  // of a block lays it out as the operand reads want it (chunk c of row
+  // r' = r % 8, e = (r / 8) % 2):
+  //   K: slot 16 (c / 2) + ((2 r' + c % 2 + e) mod 16), so the 16 rows of
+  //      one K-operand read fall in 16 different bank groups and k-step s
+  //      is a constant offset;
+  //   V: slot 16 (c / 4 + 2 (r' / 4)) + 4 (r' % 4) + c % 4, so the four
+  //      rows x four chunks of one transposed read fall in 16 different
+  //      bank groups and every V^T operand is a constant offset.
+  // Rows past the last key read a key of the request (the tile's first, or
+  // key 0 of a page past the end), so their V rows are finite: their
+  // scores are masked (every tile holding such rows is an edge tile), so P
+  // is 0 for them. ----
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t stride_bytes = PAGED ? (uint32_t)p.hkv * 16 * kD * 2   // one page
                                       : (uint32_t)p.hkv * kD * 2;       // one key
-  const char* kbase =
-      reinterpret_cast<const char*>(p.k) + 16 * ld_chunk +
-      (PAGED ? (int64_t)g * 16 * kD * 2 + (ld_row & 15) * kD * 2
-             : ((int64_t)kv_start * p.hkv + g) * kD * 2);
-  auto tile_key0 = [&](int kt) { return min(kt, n_tiles - 1) * kTile; };
-  // Paged caches: the page ids of this thread's two rows are loaded one
-  // tile before the rows themselves, so a tile's K/V loads do not wait for
-  // an id load issued in the same tile.
-  int id_a = 0, id_b = 0;
-  auto load_ids = [&](int kt) {
+  const char* kbytes = reinterpret_cast<const char*>(p.k);
+  const char* vbytes = reinterpret_cast<const char*>(p.v);
+  uint32_t koff[2], voff[2], kzero[2], vzero[2];
+  int krow[2], vrow[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int x = ((lane & 15) - e) & 15;
+    const int kc = 2 * (lane >> 4) + (x & 1);
+    const int vc = 4 * ((lane >> 4) & 1) + (lane & 3);
+    krow[e] = 8 * e + (x >> 1);
+    vrow[e] = 8 * e + 4 * (lane >> 5) + ((lane & 15) >> 2);
     if constexpr (PAGED) {
-      const int32_t* pages = p.page_indices + kv_start;
-      const int key0 = tile_key0(kt);
-      const int pg = (key0 >> 4) + (ld_row >> 4);
-      id_a = pages[key0 + ld_row < L ? pg : 0];
-      id_b = pages[key0 + 32 + ld_row < L ? pg + 2 : 0];
-    }
-  };
-  auto load_tile = [&](int kt) {
-    uint32_t ua, ub;
-    if constexpr (PAGED) {
-      (void)kt;
-      ua = (uint32_t)id_a;
-      ub = (uint32_t)id_b;
+      koff[e] = (uint32_t)g * 16 * kD * 2 + krow[e] * kD * 2 + 16 * kc;
+      voff[e] = (uint32_t)g * 16 * kD * 2 + vrow[e] * kD * 2 + 16 * vc;
+      kzero[e] = (uint32_t)g * 16 * kD * 2 + 16 * kc;
+      vzero[e] = (uint32_t)g * 16 * kD * 2 + 16 * vc;
     } else {
-      const int key0 = tile_key0(kt);
-      const int ka = key0 + ld_row, kb2 = key0 + 32 + ld_row;
-      ua = (uint32_t)(ka < L ? ka : 0);
-      ub = (uint32_t)(kb2 < L ? kb2 : 0);
+      koff[e] = (16 * wave_u + krow[e]) * stride_bytes + 16 * kc;
+      voff[e] = (16 * wave_u + vrow[e]) * stride_bytes + 16 * vc;
+      kzero[e] = 16 * kc;
+      vzero[e] = 16 * vc;
     }
-    const char* pa = kbase + (uint64_t)ua * stride_bytes;
-    const char* pb = kbase + (uint64_t)ub * stride_bytes;
-    rk0 = ld16(pa);
-    rk1 = ld16(pb);
-    rv0 = ld16(pa + vdelta);
-    rv1 = ld16(pb + vdelta);
+  }
+  // Paged caches: page ids of this wave's page in tiles first .. first + 63,
+  // one per lane; the assembly use makes the compiler wait for them here.
+  auto load_ids = [&](int first) {
+    const int kt = first + lane;
+    int id = 0;
+    if (kt < n_tiles) {
+      const int key0 = kt * kTile;
+      id = p.page_indices[kv_start + (key0 + 16 * wave_u < L ? (key0 >> 4) + wave_u : 0)];
+    }
+    asm volatile("" ::"v"(id));
+    return id;
   };
-  auto store_tile = [&](int buf, int kt) {
-    const int key0 = tile_key0(kt);
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    uint16_t* kd = lds_k + buf * kKBuf;
-    uint16_t* vd = lds_v + buf * kVBuf;
-    *reinterpret_cast<u32x4*>(kd + ld_row * kKPitch + 8 * ld_chunk) = rk0;
-    *reinterpret_cast<u32x4*>(kd + (32 + ld_row) * kKPitch + 8 * ld_chunk) = rk1;
-    *reinterpret_cast<u32x4*>(vd + ld_row * kVPitch + 8 * ld_chunk) = key0 + ld_row < L ? rv0 : z;
-    *reinterpret_cast<u32x4*>(vd + (32 + ld_row) * kVPitch + 8 * ld_chunk) =
-        key0 + 32 + ld_row < L ? rv1 : z;
+  auto issue = [&](int kt, int bf, int id) {
+    const int key0 = kt * kTile;
+    const char* kp;
+    const char* vp;
+    if constexpr (PAGED) {
+      kp = kbytes + (uint64_t)(uint32_t)id * stride_bytes;
+      vp = vbytes + (uint64_t)(uint32_t)id * stride_bytes;
+    } else {
+      (void)id;
+      const uint64_t t = ((uint64_t)(uint32_t)(kv_start + key0) * p.hkv + g) * (kD * 2);
+      kp = kbytes + t;
+      vp = vbytes + t;
+    }
+    const uint32_t kd = lds_offset(lds_k) + bf * kTileBytes + wave_u * 2048;
+    const uint32_t vd = lds_offset(lds_v) + bf * kTileBytes + wave_u * 2048;
+    const bool tail = key0 + kTile > L;   // wave-uniform
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      uint32_t ko = koff[e], vo = voff[e];
+      if (tail) {
+        const int row0 = key0 + 16 * wave_u;
+        ko = row0 + krow[e] < L ? ko : kzero[e];
+        vo = row0 + vrow[e] < L ? vo : vzero[e];
+      }
+      load_lds16(kp, ko, kd + 1024 * e);
+      load_lds16(vp, vo, vd + 1024 * e);
+    }
   };
 
-  if (n_tiles > 0) {
-    load_ids(0);
-    load_tile(0);
-    load_ids(1);
-    store_tile(0, 0);
-  }
-  __syncthreads();
+  int ids = 0;
+  if constexpr (PAGED) ids = load_ids(0);
+  // the prologue's own global loads complete here, not inside the loop
+  asm volatile("" ::"v"(bq[0][0]), "v"(bq[0][1]), "v"(bq[0][2]), "v"(bq[0][3]), "v"(bq[1][0]),
+               "v"(bq[1][1]), "v"(bq[1][2]), "v"(bq[1][3]));
+  if (n_tiles > 0) issue(0, 0, __builtin_amdgcn_readlane(ids, 0));
+  if (n_tiles > 1) issue(1, 1, __builtin_amdgcn_readlane(ids, 1));
 
   const float sl2 = p.scale_log2;
-  // transposed V reads: 16-lane group q = lane / 16 covers dims 16 (q % 2) ..
-  // of a 32-dim block and keys 4 hh + s / 4 (s = lane % 16)
-  const int tr_row = 4 * hh + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // Operand reads, byte offsets inside a tile buffer.  K operand of k-step
+  // s, key block kb: key 32 kb + r, dims 16 s + 8 hh (chunk 2 s + hh) at
+  // kread + 4096 kb + 256 s.  V^T operand: the transposed read of 16-lane
+  // group q = lane / 16 covers dims 16 (q % 2) + 4 (lane % 4) .. of a 32-dim
+  // block db (chunk 2 (q % 2) + (lane % 4) / 2 + 4 db) and key row
+  // 4 hh + (lane % 16) / 4 (+ 8 for the upper four values) of the 16-key
+  // slice hf of key block kb, at vread + 4096 kb + 2048 hf + 256 db (+ 1024).
+  const int kread = ((lane & 31) >> 3) * 1024 + 16 * ((2 * (lane & 7) + hh + ((lane >> 3) & 1)) & 15);
+  const int vread = 512 * hh + 64 * ((lane & 15) >> 2) + 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) +
+                    8 * (lane & 1);
 
   for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
-    load_tile(kt + 1);   // clamped: the last iteration repeats the last tile
-    load_ids(kt + 2);
+    const int buf = kt % kBufs;
+    // this wave's part of tile kt has landed (tile kt + 1 may be in
+    // flight); the barrier makes every part visible and frees the buffer of
+    // tile kt - 1 for tile kt + 2
+    if (kt + 1 < n_tiles) wait_vmem<4>();
+    else wait_vmem<0>();
+    barrier_only();
+    if (kt + 2 < n_tiles) {
+      if constexpr (PAGED) {
+        if (((kt + 2) & 63) == 0) ids = load_ids(kt + 2);
+      }
+      issue(kt + 2, (kt + 2) % kBufs, __builtin_amdgcn_readlane(ids, (kt + 2) & 63));
+    }
     const int key0 = kt * kTile;
     const bool wave_live = !p.causal || key0 <= wave_pos_max;
     if (wave_live) {
-      const uint16_t* kbuf = lds_k + buf * kKBuf;
-      const uint16_t* vbuf = lds_v + buf * kVBuf;
+      const char* kbuf = lds_k + buf * kTileBytes;
+      // V^T reads from one LDS address per tile, hidden from loop strength
+      // reduction, so that each read's constant part becomes its offset
+      uint32_t vaddr = lds_offset(lds_v) + buf * kTileBytes + vread;
+      asm volatile("" : "+v"(vaddr));
+      const __attribute__((address_space(3))) char* vbuf =
+          (const __attribute__((address_space(3))) char*)(uintptr_t)vaddr;
       const bool edge = (p.causal && key0 + kTile - 1 > pos_min_wg) || (key0 + kTile > L);
       const f32x16 zero16 = {};
       // K operand (A of S^T) for k-step s, key block kb: keys 32 kb + r,
       // dims 16 s + 8 hh.  V^T operand (A of O^T) for key block kb, half hf,
       // dim block db: dims 32 db + .., keys 32 kb + 16 hf + {4 hh .., 8 + 4 hh ..}.
       auto kop = [&](int s, int kb) {
-        return as_bf16x8(*reinterpret_cast<const u32x4*>(kbuf + (32 * kb + r) * kKPitch + 16 * s + 8 * hh));
+        return as_bf16x8(*reinterpret_cast<const u32x4*>(kbuf + kread + 4096 * kb + 256 * s));
       };
       auto vop = [&](int kb, int hf, int db) {
-        const uint16_t* src = vbuf + (32 * kb + 16 * hf + tr_row) * kVPitch + tr_col + 32 * db;
-        return as_bf16x8(lds_tr16_pair(src, src + 8 * kVPitch));
+        const auto* src = vbuf + 4096 * kb + 2048 * hf + 256 * db;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 1024));
+        const u32x2 a = __builtin_bit_cast(u32x2, lo), b2 = __builtin_bit_cast(u32x2, hi);
+        return as_bf16x8(u32x4{a[0], a[1], b2[0], b2[1]});
       };
       // S^T[kb][cb]: keys 32 kb + 8 (j/4) + 4 hh + j%4, column = row r of cb
       f32x16 sacc[2][2];
@@ -362,8 +406,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         o[1][db] = mfma32(vo[kb][hf][db], pb_of(1, kb, hf), o[1][db]);
       }
     }
-    store_tile(buf ^ 1, kt + 1);
-    __syncthreads();
   }
 
   // ---- epilogue: o = O / d, lse = m + log2 d (natural log at the boundary) ----

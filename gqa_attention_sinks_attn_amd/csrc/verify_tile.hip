@@ -55,45 +55,6 @@ __device__ __forceinline__ float dot2_sum(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
 }
 
-// Wait until at most N vector memory operations of this wave are
-// outstanding (the LDS-direct tile loads count among them).
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// 16 bytes per lane from global memory into LDS: lane l reads base + off
-// and writes LDS bytes lds + 16 l .. lds + 16 l + 15 (base and lds
-// wave-uniform).  Written as assembly so that the compiler neither counts
-// nor waits for these loads: wait_vmem and the workgroup barrier order
-// them against the LDS reads.
-// M0 carries the LDS address; the compiler keeps no value of its own in it
-// (the clobber is declared, the warning about it silenced).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void load_lds16(const char* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// LDS offset of a __shared__ object.
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads (which would
-// wait for every outstanding global load); the empty assembly statements
-// keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void barrier_only() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 __device__ __forceinline__ int n_chunks_of(int L, int chunk_tiles) {
   const int tiles = (L + kTile - 1) / kTile;
   return (tiles + chunk_tiles - 1) / chunk_tiles;
