@@ -55,7 +55,7 @@ EVENT_EVERY = 4                # timed decode steps between two sampled first-pa
 # 256 MiB copy; see profiles/.  Valid for the kernel sources they were taken
 # on -- reset to None whenever decode_balanced.hip or prefill.hip changes.
 DECODE_TRAFFIC_BYTES = 260_946_607
-PREFILL_TRAFFIC_BYTES = 1_882_476_635
+PREFILL_TRAFFIC_BYTES = 1_871_242_272
 
 
 def log(msg: str):
