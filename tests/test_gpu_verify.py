@@ -198,6 +198,24 @@ def test_verify_tiles_long_context_split_plan(tree):
     check(f"tiles long context tree={tree} S={S}", out, ref, lse, rl, bf16_out=bf16)
 
 
+@pytest.mark.parametrize("tree", [False, True])
+@pytest.mark.parametrize("splits", [1, 2])
+def test_verify_tiles_long_chunks(tree, splits):
+    """Chunks of more than 64 tiles on the tile kernel (one or two chunks
+    per request over caches of up to 20,003 keys): each wave reads its page
+    ids 64 tiles at a time, so a chunk's 65th and 129th tiles take a fresh
+    batch of ids, and a second chunk starts far from key 0."""
+    rng = np.random.default_rng(890 + 2 * splits + int(tree))
+    ql = [16, 24, 9]
+    b = W.make_batch(rng, kind="prefill", qlens=ql, kv_lens=[9000, 20003, 4100], hq=64, hkv=8,
+                     paged=True, sinks="normal")
+    if tree:
+        b.draft_mask = np.concatenate([W.tree_mask(W.draft_tree(rng, n)) for n in ql])
+    out, lse, bf16 = run(b, "verify", splits)
+    ref, rl = oracle.attend(b)
+    check(f"tiles long chunks tree={tree} S={splits}", out, ref, lse, rl, bf16_out=bf16)
+
+
 @pytest.mark.parametrize("splits", [0, 1, 5])
 def test_verify_tiles_group16_and_extreme_sinks(splits):
     """The tile kernel at G = 16 (64 query / 4 KV heads, 8 tokens = 128 rows)
