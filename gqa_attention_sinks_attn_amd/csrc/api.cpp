@@ -603,13 +603,15 @@ constexpr int32_t kVerifyTileRows = 128;
 constexpr int32_t kVerifyTileKeys = 64;
 constexpr int32_t kVerifyTileMaxChunks = 64;
 // Automatic chunking of the tile kernel: enough chunks of at least 8 tiles
-// (512 keys) for about kVerifyTileTargetWorkgroups workgroups if every
-// request had max_kv_len keys.  One workgroup per (request, KV head) lets
-// the longest requests bound a ragged batch; chunks cut them at the price of
-// partial writes and a merge pass (measured on 64 requests x 16 tokens, L
-// <= 4,096, 512 units: 96 us in one chunk; 72 + 9 us in two; 77 + 9 us in
-// three).
-constexpr int64_t kVerifyTileTargetWorkgroups = 1024;
+// (512 keys) for about kVerifyTileTargetItems (request, KV head, chunk)
+// items if every request had max_kv_len keys; each item runs one workgroup
+// per 128-row tile.  One item per (request, KV head) lets the longest
+// requests bound a ragged batch; chunks cut them at the price of partial
+// writes and a merge pass.  Measured on 64 requests (L <= 4,096, 512
+// (request, KV head) pairs): 16-token drafts 0.089 ms in one chunk, 0.077
+// in two, 0.080 in three; 32-token trees (two row tiles) 0.144, 0.136 and
+// 0.139 -- two chunks in both, whatever the row tiles.
+constexpr int64_t kVerifyTileTargetItems = 1024;
 constexpr int32_t kVerifyTileMinChunkTiles = 8;
 
 bool verify_uses_tiles(int32_t group, int32_t columns) {
@@ -630,8 +632,8 @@ TilePlan verify_tile_plan(int32_t batch, int32_t hkv, int32_t columns, int32_t m
   if (requested > 0) {
     want = requested;
   } else {
-    const int64_t units = (int64_t)batch * hkv * tp.row_tiles;
-    want = units > 0 ? (kVerifyTileTargetWorkgroups + units - 1) / units : 1;
+    const int64_t pairs = (int64_t)batch * hkv;
+    want = pairs > 0 ? (kVerifyTileTargetItems + pairs - 1) / pairs : 1;
     const int64_t by_len = tiles / kVerifyTileMinChunkTiles;
     if (want > by_len) want = by_len;
   }

@@ -328,8 +328,8 @@ sink_attn_status sink_attn_decode_balanced_finish(
  *                    64: one chunk per request when the grid already holds
  *                    >= 256 workgroups, else enough chunks of >= 16 pages
  *                    for about 512.  C > 64: chunks of >= 512 keys towards
- *                    1,024 workgroups of (request, KV head, 128-pair
- *                    group, chunk), at most 64 chunks.
+ *                    1,024 (request, KV head, chunk) items (each one
+ *                    workgroup per 128-pair group), at most 64 chunks.
  *                    S > 0: S chunks per request of ceil(max_kv_len / S)
  *                    keys, rounded up to a multiple of 16 (C <= 64) or of
  *                    64 (C > 64; at most 64 chunks); a chunk past a

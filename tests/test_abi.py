@@ -366,16 +366,16 @@ def test_verify_plan_and_workspace():
     # 8-token drafts at G = 8: 64 pairs = 2 groups of 32 -> 4 chunks
     assert nsp(8, 64, 8, 8, 4096, 0) == 4
     # past 64 pairs per KV head the tile kernel runs: 128-row tiles, chunks
-    # of >= 8 tiles (512 keys) towards 1,024 workgroups
-    assert nsp(64, 64, 8, 16, 4096, 0) == 2          # 512 units
-    assert nsp(128, 64, 8, 16, 4096, 0) == 1         # 1,024 units: one chunk
+    # of >= 8 tiles (512 keys) towards 1,024 (request, KV head, chunk) items
+    assert nsp(64, 64, 8, 16, 4096, 0) == 2          # 512 (request, KV head) pairs
+    assert nsp(128, 64, 8, 16, 4096, 0) == 1         # 1,024 pairs: one chunk
     assert sa.sink_attn_verify_workspace_size(128, 64, 8, 64, 2048, 16, 4096, 0) == 0
-    assert nsp(64, 64, 8, 32, 4096, 0) == 1          # 2 row tiles x 512 units
-    assert nsp(8, 64, 8, 16, 4096, 0) == 8           # 64 units, 64 tiles
-    assert nsp(2, 64, 8, 32, 4096, 0) == 8           # 32 units (2 row tiles)
-    assert nsp(2, 64, 4, 32, 4096, 0) == 8           # G = 16: 4 row tiles, 32 units
+    assert nsp(64, 64, 8, 32, 4096, 0) == 2          # 512 pairs, whatever the 2 row tiles
+    assert nsp(8, 64, 8, 16, 4096, 0) == 8           # 64 pairs, 64 tiles
+    assert nsp(2, 64, 8, 32, 4096, 0) == 8           # 16 pairs (2 row tiles)
+    assert nsp(2, 64, 4, 32, 4096, 0) == 8           # G = 16: 4 row tiles, 8 pairs
     assert nsp(8, 64, 8, 16, 300, 0) == 1            # 5 tiles: too short to split
-    assert nsp(2, 64, 8, 16, 131072, 0) == 64        # 16 units -> 64 chunks of 32 tiles
+    assert nsp(2, 64, 8, 16, 131072, 0) == 64        # 16 pairs -> 64 chunks of 32 tiles
     # at most 64 chunks: an explicit request is capped there
     assert nsp(1, 64, 8, 16, 131072, 1000) == 64
     S = nsp(2, 64, 8, 32, 4096, 0)
