@@ -150,10 +150,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   //   V: slot 16 (c / 4 + 2 (r' / 4)) + 4 (r' % 4) + c % 4, so the four
   //      rows x four chunks of one transposed read fall in 16 different
   //      bank groups and every V^T operand is a constant offset.
-  // Rows past the last key read a key of the request (the tile's first, or
-  // key 0 of a page past the end), so their V rows are finite: their
-  // scores are masked (every tile holding such rows is an edge tile), so P
-  // is 0 for them. ----
+  // Rows past the last key read a key of the request, so their V rows are
+  // finite: the first row of their page (a page past the end is replaced by
+  // the request's first page) or, on a contiguous cache, the tile's first
+  // key.  Their scores are masked (every tile holding such rows is an edge
+  // tile), so P is 0 for them. ----
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t stride_bytes = PAGED ? (uint32_t)p.hkv * 16 * kD * 2   // one page
                                       : (uint32_t)p.hkv * kD * 2;       // one key

@@ -149,8 +149,9 @@ void verify_tile_kernel(VerifyTileArgs p) {
   //   V: slot 16 (c / 4 + 2 (r' / 4)) + 4 (r' % 4) + c % 4, so the four
   //      rows x four chunks of one transposed read fall in 16 different
   //      bank groups and every V^T operand is a constant offset.
-  // Rows past the last key read key 0 (a key of the request, so finite):
-  // their scores are masked, so P is 0 for them. ----
+  // Rows past the last key read the first row of their page (a page past
+  // the request's end is replaced by its first page), a key of the request
+  // and so finite: their scores are masked, so P is 0 for them. ----
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t page_bytes = (uint32_t)p.hkv * 16 * kD * 2;   // one page, every KV head
   const char* kbytes = reinterpret_cast<const char*>(p.k);
