@@ -198,6 +198,32 @@ def test_verify_tiles_long_context_split_plan(tree):
     check(f"tiles long context tree={tree} S={S}", out, ref, lse, rl, bf16_out=bf16)
 
 
+@pytest.mark.parametrize("qlens,tree", [([4, 3, 4], False),            # column kernel
+                                         ([16, 24, 9], False),          # tile kernel
+                                         ([16, 24, 9], True)])
+@pytest.mark.parametrize("splits", [0, 2])
+def test_verify_nan_tails_do_not_leak(qlens, tree, splits):
+    """NaN bit patterns in the unused slots of each request's last page
+    (never read by the definition) must not reach the output: the tile
+    kernel's rows past the last key read a key of the request instead, and
+    their probabilities are 0; the column kernel masks them."""
+    rng = np.random.default_rng(910 + 3 * splits + int(tree) + qlens[0])
+    L = [40, 57, 1013]                     # every last page part-used
+    b = W.make_batch(rng, kind="prefill", qlens=qlens, kv_lens=L, hq=64, hkv=8, paged=True,
+                     sinks="normal")
+    if tree:
+        b.draft_mask = np.concatenate([W.tree_mask(W.draft_tree(rng, n)) for n in qlens])
+    for r, n in enumerate(b.kv_len):
+        used = int(n) % 16
+        if used:
+            last = b.page_indices[b.kv_indptr[r + 1] - 1]
+            b.k[last, :, used:, :] = 0x7FC0  # NaN
+            b.v[last, :, used:, :] = 0x7FC0
+    out, lse, bf16 = run(b, "verify", splits)
+    ref, rl = oracle.attend(b)
+    check(f"NaN tails qlens={qlens} tree={tree} S={splits}", out, ref, lse, rl, bf16_out=bf16)
+
+
 @pytest.mark.parametrize("tree", [False, True])
 @pytest.mark.parametrize("splits", [1, 2])
 def test_verify_tiles_long_chunks(tree, splits):
