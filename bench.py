@@ -1,40 +1,46 @@
 #!/usr/bin/env python3
 """Benchmark of the sink-attention hot path on one MI355X.
 
-Default workload: paged decode, batch 64, KV lengths uniform in [1, 4096],
-64 query / 8 KV heads, head_dim 64, 16-token pages with a permuted page table
-(the decode workload the headline metric is quoted on).  One step = one
-pass of the decode path the library's automatic plan takes for it: the
-load-balanced first pass (sink_attn_decode_balanced_partial, every wave
-streaming an equal share of the batch's pages) followed by its finish pass
-(sink_attn_decode_balanced_finish, the LSE merge of requests that span
-several ranges), both through the C ABI.  Metric: KV bytes read per second
-(2 * Hkv * 64 * 2 B per KV token) over the whole step.  --decode-plan
-chunked times the split-KV pair (sink_attn_decode_partial +
-sink_attn_merge) instead.
+Headline workload (the JSON line's `value`): paged decode, batch 64, KV
+lengths uniform in [1, 4096], 64 query / 8 KV heads, head_dim 64, 16-token
+pages with a permuted page table.  One step = one pass of the decode path
+the library's automatic plan takes for it: the load-balanced first pass
+(sink_attn_decode_balanced_partial, every wave streaming an equal share of
+the batch's pages) followed by its finish pass (sink_attn_decode_balanced_
+finish, the LSE merge of requests that span several ranges), both through
+the C ABI.  `value` = KV bytes read per second (2 * Hkv * 64 * 2 B per KV
+token) over the whole step.  --decode-plan chunked times the split-KV pair
+(sink_attn_decode_partial + sink_attn_merge) instead.
 
-Also reported, on the same JSON line:
-  * "roofline": the dominant kernel (the first pass) -- algorithmic bytes
-    per launch / its mean launch time from HIP events around it on its own
-    stream (every fourth launch of the timed region), against the 8 TB/s
-    HBM peak; "traffic" from rocprofv3 counters when a measurement for the
-    current kernel exists, else null;
+Also on the same JSON line, every one on the same seeded inputs the parity
+tests use:
+  * "roofline": the headline step's dominant kernel (the first pass):
+    algorithmic bytes per launch / its mean launch time from HIP events on
+    the stream it runs on (every fourth launch of the timed region), against
+    the 8 TB/s HBM peak;
   * "prefill": the causal prefill workload (8 x 4096 tokens, 64/8 heads,
     contiguous KV) in TFLOP/s against the 2.5 PFLOP/s dense bf16 peak;
-  * "cpu_baseline": the fp64 oracle timed on this host's cores on the same
-    decode batch.
+  * "workloads": the long split-KV decode (4 x 131,072 keys, 32 chunks
+    merged by LSE, sinks of standard deviation 2) and the two calls of the
+    mixed ragged batch (16 chunked prefills on cached prefixes, then 256
+    decodes), each with its own roofline, plus the two mixed calls back to
+    back on one stream;
+  * "cpu_baseline": the fp64 oracle timed on this host's cores: the whole
+    decode batch (repeated), a bounded block of the causal prefill, the tiny
+    prefill, single-thread times and the CPU model.
+
+`traffic` (HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
+passes over `--mode traffic`, each scaled by the same counter on a 256 MiB
+copy) is reported only while the kernel sources hash to the values the
+counters were taken on; otherwise null.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
     python bench.py --mode traffic   # kernels only, for rocprofv3 --pmc passes
-
---mode traffic runs, untimed: a plain 256 MiB device-to-device copy three
-times (the calibration dispatch for FETCH_SIZE / WRITE_SIZE), then the decode
-first pass eight times on the decode workload (rotating the same four KV
-copies as the timed run), then the prefill kernel three times.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -49,27 +55,53 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 KV_COPIES = 4                  # rotated KV pools: 4 x 269 MB > 256 MB last-level cache
 EVENT_EVERY = 4                # timed decode steps between two sampled first-pass launches
+CSRC = os.path.join(ROOT, "gqa_attention_sinks_attn_amd", "csrc")
 
-# HBM bytes per dispatch from rocprofv3 FETCH_SIZE + WRITE_SIZE passes
-# (python bench.py --mode traffic), each scaled by the same counter on a
-# 256 MiB copy; see profiles/.  Valid for the kernel sources they were taken
-# on -- reset to None whenever decode_balanced.hip or prefill.hip changes.
-DECODE_TRAFFIC_BYTES = 260_946_607
-PREFILL_TRAFFIC_BYTES = 1_871_242_272
+# HBM bytes per dispatch (FETCH_SIZE + WRITE_SIZE, scaled by the 256 MiB
+# copy's counters; profiles/ holds the summaries and commands), keyed by the
+# kernel and by the hash of the sources that build it.  A source change
+# makes the figure stale: it is then reported as null until retaken.
+TRAFFIC = {
+    "decode_balanced": (260_946_607, "decode_balanced.hip", "e0a3f331d123b616"),
+    "prefill": (None, "prefill.hip", ""),
+}
+
+
+def sources_hash(main: str) -> str:
+    h = hashlib.sha256()
+    for f in (main, "common.hpp", "launch.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_of(kernel: str):
+    nbytes, main, digest = TRAFFIC[kernel]
+    if nbytes is None or sources_hash(main) != digest:
+        return None
+    return nbytes
 
 
 def log(msg: str):
     print(msg, file=sys.stderr, flush=True)
 
 
-def decode_algorithmic_bytes(b) -> int:
-    """Bytes the definition must read once: K and V of every KV token
-    (2 * Hkv * D * 2 B each), the queries, page ids and per-request lengths."""
+def decode_algorithmic_bytes(b, out_elem_bytes: int = 4) -> int:
+    """Bytes the definition reads and writes once: K and V of every KV token
+    (2 * Hkv * D * 2 B each), the queries, the output rows and their LSE,
+    page ids, per-request lengths and page offsets, and the sinks."""
     L = b.kv_len.astype(np.int64)
     kv = int(L.sum()) * 2 * b.num_kv_heads * b.head_dim * 2
-    q = int(b.qo_indptr[-1]) * b.num_qo_heads * b.head_dim * 2   # query rows
+    rows = int(b.qo_indptr[-1]) * b.num_qo_heads
+    q = rows * b.head_dim * 2
+    out = rows * b.head_dim * out_elem_bytes + rows * 4
     pages = int(((L + b.page_size - 1) // b.page_size).sum()) * 4
-    return kv + q + pages + b.batch * 8
+    sinks = b.num_qo_heads * 4 if b.sinks is not None else 0
+    return kv + q + out + pages + b.batch * 4 + (b.batch + 1) * 4 + sinks
+
+
+def kv_bytes_of(b) -> int:
+    return int(b.kv_len.astype(np.int64).sum()) * 2 * b.num_kv_heads * b.head_dim * 2
 
 
 def prefill_pairs(b) -> int:
@@ -81,22 +113,30 @@ def prefill_pairs(b) -> int:
     return int(per_req.sum()) * b.num_qo_heads
 
 
-def bench_decode(args, torch, sa, device, W):
-    b = W.config(2)
-    balanced = args.decode_plan == "balanced"
+def prefill_flops(b) -> int:
+    return prefill_pairs(b) * 4 * b.head_dim
+
+
+# ------------------------------------------------------------------ decode
+
+def time_decode(torch, sa, device, b, steps, warmup, balanced=True, kv_copies=1,
+                event_every=1):
+    """Times the decode of batch b: the first pass (events around every
+    `event_every`-th launch, on the stream it runs on) and the whole step
+    (first pass + finish, events around the timed region)."""
     db = device.to_device(b, plan="balanced" if balanced else "chunked")
     B, Hq, D = db.batch, db.num_qo_heads, db.head_dim
     out_code = sa.F32 if db.out.dtype == torch.float32 else sa.BF16
     if balanced:
-        R = sa.sink_attn_decode_num_ranges(B, db.num_kv_heads, db.max_kv_len, 0)
-        plan = dict(num_ranges=R)
+        plan = dict(num_ranges=sa.sink_attn_decode_num_ranges(B, db.num_kv_heads,
+                                                               db.max_kv_len, 0))
     else:
         S = device.splits_of(db)
         o_parts = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
         lse_parts = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
         plan = dict(num_splits=S)
-    ks = [db.k] + [db.k.clone() for _ in range(KV_COPIES - 1)]
-    vs = [db.v] + [db.v.clone() for _ in range(KV_COPIES - 1)]
+    ks = [db.k] + [db.k.clone() for _ in range(kv_copies - 1)]
+    vs = [db.v] + [db.v.clone() for _ in range(kv_copies - 1)]
     torch.cuda.synchronize()
 
     def first(k, v):
@@ -120,7 +160,7 @@ def bench_decode(args, torch, sa, device, W):
             sa.sink_attn_merge(o_parts, lse_parts, B, Hq, S, D, db.out, out_code, db.lse)
 
     def step(i, ev=None):
-        k, v = ks[i % KV_COPIES], vs[i % KV_COPIES]
+        k, v = ks[i % kv_copies], vs[i % kv_copies]
         if ev is not None:
             ev[0].record()
         first(k, v)
@@ -128,32 +168,122 @@ def bench_decode(args, torch, sa, device, W):
             ev[1].record()
         second()
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # The first pass is bracketed by events on every EVENT_EVERY-th step of
-    # the timed region: each pair of event records costs the stream a few
-    # microseconds, which would otherwise be charged to every step.
-    sampled = [i for i in range(args.steps) if i % EVENT_EVERY == 0]
+    # Each pair of event records costs the stream a few microseconds, so on
+    # a short kernel only every event_every-th step is bracketed.
+    sampled = [i for i in range(steps) if i % event_every == 0]
     evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for i in sampled}
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, evs.get(i))
     t1.record()
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
+    ms_step = t0.elapsed_time(t1) / steps
     kern_ms = float(np.mean([a.elapsed_time(c) for a, c in evs.values()]))
-    kv_bytes = int(b.kv_len.astype(np.int64).sum()) * 2 * b.num_kv_heads * b.head_dim * 2
-    alg = decode_algorithmic_bytes(b)
-    ms_step = total_ms / args.steps
-    res = dict(batch=b, db=db, plan=plan, ms_step=ms_step, kern_ms=kern_ms,
-               kern_samples=len(evs), kv_bytes=kv_bytes,
-               alg_bytes=alg, value=kv_bytes / (ms_step * 1e-3) / 1e9, first=first)
+    res = dict(db=db, plan=plan, ms_step=ms_step, kern_ms=kern_ms, kern_samples=len(evs),
+               kv_bytes=kv_bytes_of(b), alg_bytes=decode_algorithmic_bytes(b),
+               first=first, ks=ks, vs=vs)
     return res
+
+
+def decode_entry(name, b, r, kernel, traffic=None):
+    """JSON object of one timed decode workload."""
+    achieved = r["alg_bytes"] / (r["kern_ms"] * 1e-3) / 1e9
+    whole = r["alg_bytes"] / (r["ms_step"] * 1e-3) / 1e9
+    return {
+        "workload": name, **r["plan"],
+        "call": "sink_attn_decode_balanced_partial + sink_attn_decode_balanced_finish "
+                "(the automatic plan of sink_attn_decode)",
+        "ms_per_call": round(r["ms_step"], 5),
+        "kv_gbs": round(r["kv_bytes"] / (r["ms_step"] * 1e-3) / 1e9, 1),
+        "whole_call_frac_hbm": round(whole / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": kernel, "kernel_ms": round(r["kern_ms"], 5),
+            "kernel_samples": r["kern_samples"], "algorithmic_bytes": r["alg_bytes"],
+        },
+    }
+
+
+# ----------------------------------------------------------------- prefill
+
+def time_prefill(torch, device, b, steps, warmup):
+    db = device.to_device(b, with_lse=False)
+    torch.cuda.synchronize()
+    for _ in range(max(1, warmup)):
+        device.run(db)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        device.run(db)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(c) for a, c in evs]))
+    return db, ms
+
+
+def prefill_entry(name, b, ms, steps, traffic=None):
+    flops = prefill_flops(b)
+    tfs = flops / (ms * 1e-3) / 1e12
+    return dict(workload=name, call="sink_attn_prefill", value=round(tfs, 2), unit="TFLOP/s",
+                ms_per_call=round(ms, 4), flop_per_call=flops, steps=steps,
+                roofline=dict(bound="mfma", achieved=round(tfs, 2), peak=BF16_PEAK_TFLOPS,
+                              unit="TFLOP/s", frac=round(tfs / BF16_PEAK_TFLOPS, 4),
+                              traffic=traffic, kernel=f"prefill_kernel<{b.num_qo_heads // b.num_kv_heads}, "
+                                                      f"{'true' if b.page_indices is not None else 'false'}>"))
+
+
+def bench_workloads(args, torch, sa, device, W):
+    """Workloads 3 and 5, each with its own roofline."""
+    out = {}
+    steps = max(5, min(args.steps, 20))
+    warm = max(1, args.warmup)
+    log("[bench] workload 3: long split-KV decode")
+    b3 = W.config(3)
+    r3 = time_decode(torch, sa, device, b3, steps, warm)
+    out["c3_split_decode"] = decode_entry(W.CONFIG_NAMES[3], b3, r3,
+                                          "decode_balanced_kernel<8> (first pass)")
+    out["c3_split_decode"]["note"] = (
+        "the 32 chunks of the workload are the page ranges of the automatic plan; "
+        "the split-KV pair with S = 32 is timed under extra")
+    del r3
+    torch.cuda.empty_cache()
+
+    log("[bench] workload 5: mixed ragged batch")
+    mx = W.config(5)
+    pdb, pms = time_prefill(torch, device, mx.prefill, steps, warm)
+    out["c5_prefill"] = prefill_entry(W.CONFIG_NAMES[5] + " -- (i) chunked prefills",
+                                      mx.prefill, pms, steps)
+    r5 = time_decode(torch, sa, device, mx.decode, steps, warm)
+    out["c5_decode"] = decode_entry(W.CONFIG_NAMES[5] + " -- (ii) decodes", mx.decode, r5,
+                                    "decode_balanced_kernel<8> (first pass)")
+    # both calls back to back on one stream, as one step of the mixed batch
+    ddb = r5["db"]
+
+    def both(i):
+        device.run(pdb)
+        device.run(ddb)
+    seq_ms = _time_calls(torch, both, steps, warm)
+    flops = prefill_flops(mx.prefill)
+    kvb = kv_bytes_of(mx.decode)
+    out["c5_sequential"] = dict(
+        call="sink_attn_prefill then sink_attn_decode (automatic plan), one stream",
+        ms_per_step=round(seq_ms, 4),
+        sum_of_calls_ms=round(pms + r5["ms_step"], 4),
+        prefill_tflops_share=round(flops / (seq_ms * 1e-3) / 1e12, 2),
+        decode_kv_gbs_share=round(kvb / (seq_ms * 1e-3) / 1e9, 1))
+    del pdb, r5, ddb, mx
+    torch.cuda.empty_cache()
+    return out
 
 
 def _time_calls(torch, fn, steps, warmup):
@@ -171,51 +301,133 @@ def _time_calls(torch, fn, steps, warmup):
     return float(np.mean([a.elapsed_time(c) for a, c in evs]))
 
 
-def kv_bytes_of(b) -> int:
-    return int(b.kv_len.astype(np.int64).sum()) * 2 * b.num_kv_heads * b.head_dim * 2
+# -------------------------------------------------------------- CPU oracle
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(W, dec_batch, seconds):
+    """The oracle as it stands (fp64, OpenMP over (row, head)), timed on this
+    host: the whole decode batch repeated for about `seconds`; a contiguous
+    block of causal-prefill rows (all heads) sized to about `seconds`; the
+    tiny prefill (mean of 10); single-thread times of the tiny prefill and
+    the decode batch; the long split decode once."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    steady = time.perf_counter
+
+    def timed(fn):
+        t = steady()
+        fn()
+        return steady() - t
+
+    # decode (the headline workload), whole batch, repeated
+    times = []
+    t_end = steady() + seconds
+    while True:
+        times.append(timed(lambda: oracle.attend(dec_batch, nthreads=threads)))
+        if steady() >= t_end or len(times) >= 1000:
+            break
+    dec_mean = float(np.mean(times))
+    kvb = kv_bytes_of(dec_batch)
+    L = dec_batch.kv_len.astype(np.int64)
+    dec_flops = int(L.sum()) * dec_batch.num_qo_heads * 4 * dec_batch.head_dim
+
+    # prefill: rows of one request of the causal prefill workload, all heads,
+    # in row order (the oracle's own traversal), from its last row backwards
+    # until the block holds about `seconds` of work at a probed rate
+    b4 = W.config(4)
+    qlen = int(b4.qo_indptr[1] - b4.qo_indptr[0])
+    probe_rows = 64
+    rows = np.repeat(np.arange(qlen - probe_rows, qlen, dtype=np.int64), b4.num_qo_heads)
+    heads = np.tile(np.arange(b4.num_qo_heads, dtype=np.int32), probe_rows)
+    t_probe = timed(lambda: oracle.attend_rows(b4, rows, heads, nthreads=threads))
+    n_rows = int(min(qlen, max(probe_rows, probe_rows * seconds / max(t_probe, 1e-3))))
+    r0 = qlen - n_rows
+    rows = np.repeat(np.arange(r0, qlen, dtype=np.int64), b4.num_qo_heads)
+    heads = np.tile(np.arange(b4.num_qo_heads, dtype=np.int32), n_rows)
+    t_pre = timed(lambda: oracle.attend_rows(b4, rows, heads, nthreads=threads))
+    # query t of a 4096-token request sees t + 1 keys
+    pre_flops = int(np.arange(r0 + 1, qlen + 1, dtype=np.int64).sum()) * b4.num_qo_heads \
+        * 4 * b4.head_dim
+    pre_rate = pre_flops / t_pre
+    c4_flops = prefill_flops(b4)
+    del b4
+
+    b1 = W.config(1)
+    c1_flops = prefill_flops(b1)
+    c1_mean = float(np.mean([timed(lambda: oracle.attend(b1, nthreads=threads))
+                             for _ in range(10)]))
+    c1_single = float(np.mean([timed(lambda: oracle.attend(b1, nthreads=1)) for _ in range(10)]))
+    c2_single = timed(lambda: oracle.attend(dec_batch, nthreads=1))
+
+    b3 = W.config(3)
+    c3_s = timed(lambda: oracle.attend(b3, nthreads=threads))
+    c3_flops = int(b3.kv_len.astype(np.int64).sum()) * b3.num_qo_heads * 4 * b3.head_dim
+    del b3
+
+    return dict(
+        value=round(kvb / dec_mean / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
+        sample=f"the whole decode batch (64 requests, {int(L.sum())} KV tokens, all 64 heads), "
+               f"fp64, {len(times)} run(s), mean {dec_mean:.3f} s",
+        cpu_model=cpu_model(),
+        prefill=dict(
+            value=round(pre_rate / 1e9, 3), unit="GFLOP/s", cores=threads, kind="oracle",
+            sample=f"causal prefill 8 x 4096, 64q/8kv: rows {r0}..{qlen - 1} of request 0, all "
+                   f"64 heads ({pre_flops / 1e9:.1f} GFLOP) in {t_pre:.2f} s",
+            whole_workload_s_at_this_rate=round(c4_flops / pre_rate, 1)),
+        per_workload=dict(
+            c1_s=round(c1_mean, 5), c1_gflops=round(c1_flops / c1_mean / 1e9, 3),
+            c2_s=round(dec_mean, 4), c2_gflops=round(dec_flops / dec_mean / 1e9, 3),
+            c3_s=round(c3_s, 3), c3_gflops=round(c3_flops / c3_s / 1e9, 3)),
+        single_thread=dict(c1_s=round(c1_single, 5), c2_s=round(c2_single, 3)),
+    )
+
+
+# ------------------------------------------------------------------ extras
 
 def bench_extra(args, torch, sa, device, W):
-    """The other workloads, each timed whole (all kernels of the call), HIP
-    events: the long split decode (workload 3), both calls of the mixed batch
-    (workload 5), a multi-token verification batch (64 requests, 4 drafted
-    tokens each, KV lengths U[4, 4096]) through sink_attn_prefill and
-    sink_attn_verify, and 16-token drafts (linear, then random trees) through
-    sink_attn_verify and sink_attn_verify_tree, the bias + rotary +
-    paged-append step on a prefill and a decode step, and a whole decode
-    step (append + attend) eager and replayed from a captured graph."""
+    """Other batches, each timed whole (all kernels of the call), HIP events:
+    the split-KV pair on the long decode, a multi-token verification batch
+    (64 requests, 4 drafted tokens each, KV lengths U[4, 4096]) through
+    sink_attn_prefill and sink_attn_verify, and 16-token drafts (linear,
+    then random trees) through sink_attn_verify and sink_attn_verify_tree,
+    the bias + rotary + paged-append step on a prefill and a decode step,
+    and a whole decode step (append + attend) eager and replayed from a
+    captured graph."""
     res = {}
     steps, warm = max(5, min(args.steps, 20)), max(1, args.warmup)
 
-    def decode_line(name, b):
-        db = device.to_device(b, plan="balanced")
-        ms = _time_calls(torch, lambda i: device.run(db), steps, warm)
-        gbs = kv_bytes_of(b) / (ms * 1e-3) / 1e9
-        alg = decode_algorithmic_bytes(b) / (ms * 1e-3) / 1e9
-        res[name] = dict(workload=b.name, call="sink_attn_decode (automatic plan: balanced)",
-                         ms_per_call=round(ms, 5), kv_gbs=round(gbs, 1),
-                         frac_hbm=round(alg / HBM_PEAK_GBS, 4))
-        del db
-        torch.cuda.empty_cache()
+    log("[bench] extra: workload 3 through the split-KV pair (32 chunks, then the merge)")
+    b3 = W.config(3)
+    db3 = device.to_device(b3, plan="chunked")
+    ms = _time_calls(torch, lambda i: device.run(db3), steps, warm)
+    res["c3_split_kv_pair"] = dict(workload=b3.name, call="sink_attn_decode (num_splits = 32)",
+                                   ms_per_call=round(ms, 5),
+                                   kv_gbs=round(kv_bytes_of(b3) / (ms * 1e-3) / 1e9, 1),
+                                   frac_hbm=round(decode_algorithmic_bytes(b3) / (ms * 1e-3)
+                                                  / 1e9 / HBM_PEAK_GBS, 4))
+    del db3, b3
+    torch.cuda.empty_cache()
 
     def prefill_line(name, b, call="sink_attn_prefill"):
         db = device.to_device(b, with_lse=False)
         ms = _time_calls(torch, lambda i: device.run(db), steps, warm)
-        flops = prefill_pairs(b) * 4 * b.head_dim
-        tfs = flops / (ms * 1e-3) / 1e12
+        tfs = prefill_flops(b) / (ms * 1e-3) / 1e12
         res[name] = dict(workload=b.name, call=call, ms_per_call=round(ms, 5),
                          tflops=round(tfs, 2), frac_mfma=round(tfs / BF16_PEAK_TFLOPS, 4),
                          kv_gbs=round(kv_bytes_of(b) / (ms * 1e-3) / 1e9, 1))
         del db
         torch.cuda.empty_cache()
 
-    log("[bench] extra: workload 3")
-    decode_line("c3_split_decode", W.config(3))
-    log("[bench] extra: workload 5")
-    mx = W.config(5)
-    prefill_line("c5_prefill", mx.prefill)
-    decode_line("c5_decode", mx.decode)
-    del mx
     log("[bench] extra: verification batch")
     vb = W.verify_workload("verify_4tok")
     prefill_line("verify_4tok_prefill", vb, call="sink_attn_prefill (qlen 4 per request)")
@@ -223,8 +435,8 @@ def bench_extra(args, torch, sa, device, W):
     def verify_line(name, b, call):
         db = device.to_device(b, with_lse=False, plan="verify")
         ms = _time_calls(torch, lambda i: device.run(db), steps, warm)
-        # reads as a decode, plus the output rows written (fp32)
-        alg = decode_algorithmic_bytes(b) + b.total_q * b.num_qo_heads * b.head_dim * 4
+        # reads as a decode (the output rows fp32, no LSE)
+        alg = decode_algorithmic_bytes(b) - b.total_q * b.num_qo_heads * 4
         res[name] = dict(
             workload=b.name, call=call, ms_per_call=round(ms, 5),
             kv_gbs=round(kv_bytes_of(b) / (ms * 1e-3) / 1e9, 1),
@@ -327,87 +539,63 @@ def append_lines(args, torch, sa, W, res, steps, warm):
         torch.cuda.empty_cache()
 
 
-def bench_prefill(args, torch, sa, device, W):
-    b = W.config(4)
-    db = device.to_device(b, with_lse=False)
-    torch.cuda.synchronize()
-    steps = max(5, min(args.steps, 20))
-    for _ in range(max(1, args.warmup)):
-        device.run(db)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for i in range(steps):
-        evs[i][0].record()
-        device.run(db)
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(c) for a, c in evs]))
-    flops = prefill_pairs(b) * 4 * b.head_dim
-    tfs = flops / (ms * 1e-3) / 1e12
-    return dict(workload=W.CONFIG_NAMES[4], value=round(tfs, 2), unit="TFLOP/s",
-                ms_per_call=round(ms, 4), flop_per_call=flops, steps=steps,
-                roofline=dict(bound="mfma", achieved=round(tfs, 2), peak=BF16_PEAK_TFLOPS,
-                              unit="TFLOP/s", frac=round(tfs / BF16_PEAK_TFLOPS, 4),
-                              traffic=PREFILL_TRAFFIC_BYTES))
-
-
-def cpu_baseline(b, kv_bytes, seconds):
-    import oracle
-    threads = len(os.sched_getaffinity(0))
-    times = []
-    t_end = time.perf_counter() + seconds
-    while True:
-        t = time.perf_counter()
-        oracle.attend(b, nthreads=threads)
-        times.append(time.perf_counter() - t)
-        if time.perf_counter() >= t_end or len(times) >= 1000:
-            break
-    mean = float(np.mean(times))
-    return dict(value=round(kv_bytes / mean / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
-                sample=f"the whole decode batch (64 requests, {int(b.kv_len.sum())} KV tokens, "
-                       f"all 64 heads), fp64, {len(times)} run(s), mean {mean:.3f} s")
-
+# ----------------------------------------------------------------- traffic
 
 def traffic_run(torch, sa, device, W):
-    """Untimed dispatches for hardware-counter passes (see module doc)."""
+    """Untimed dispatches for hardware-counter passes, in this order: a plain
+    256 MiB device-to-device copy three times (the calibration dispatch for
+    FETCH_SIZE / WRITE_SIZE), the headline decode's first pass eight times
+    (rotating the same four KV copies as the timed run), the causal prefill
+    three times, the long split decode's first pass three times, then the
+    mixed batch's prefill and decode first pass three times each."""
     x = torch.ones(256 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     y = torch.empty_like(x)
     for _ in range(3):
         y.copy_(x)
     torch.cuda.synchronize()
     log(f"[traffic] copy: {x.numel() * 4} bytes read and written per dispatch")
+    del x, y
     b = W.config(2)
-    db = device.to_device(b, plan="balanced")
-    B, Hq, D = db.batch, db.num_qo_heads, db.head_dim
-    out_code = sa.F32 if db.out.dtype == torch.float32 else sa.BF16
-    ks = [db.k] + [db.k.clone() for _ in range(KV_COPIES - 1)]
-    vs = [db.v] + [db.v.clone() for _ in range(KV_COPIES - 1)]
-    for i in range(8):
-        sa.sink_attn_decode_balanced_partial(
-            db.q, ks[i % KV_COPIES], vs[i % KV_COPIES], db.kv_indptr, db.page_indices, db.kv_len,
-            db.sinks, B, Hq, db.num_kv_heads, D, db.page_size, db.max_kv_len, 0, db.sm_scale,
-            db.out, out_code, db.lse, db.workspace, db.workspace_bytes)
-    torch.cuda.synchronize()
-    log(f"[traffic] decode first pass: {decode_algorithmic_bytes(b)} algorithmic bytes per dispatch")
+    r = time_decode(torch, sa, device, b, steps=8, warmup=0, kv_copies=KV_COPIES)
+    log(f"[traffic] decode first pass x8: {decode_algorithmic_bytes(b)} algorithmic bytes")
+    del r
     pb = W.config(4)
     pdb = device.to_device(pb, with_lse=False)
     for _ in range(3):
         device.run(pdb)
     torch.cuda.synchronize()
-    log(f"[traffic] prefill: {prefill_pairs(pb) * 4 * pb.head_dim} flop per dispatch")
+    log(f"[traffic] prefill x3: {prefill_flops(pb)} flop per dispatch")
+    del pdb, pb
+    b3 = W.config(3)
+    r = time_decode(torch, sa, device, b3, steps=3, warmup=0)
+    log(f"[traffic] long decode first pass x3: {decode_algorithmic_bytes(b3)} algorithmic bytes")
+    del r, b3
+    mx = W.config(5)
+    pdb = device.to_device(mx.prefill, with_lse=False)
+    for _ in range(3):
+        device.run(pdb)
+    torch.cuda.synchronize()
+    log(f"[traffic] mixed prefill x3: {prefill_flops(mx.prefill)} flop per dispatch")
+    r = time_decode(torch, sa, device, mx.decode, steps=3, warmup=0)
+    log(f"[traffic] mixed decode first pass x3: {decode_algorithmic_bytes(mx.decode)} "
+        f"algorithmic bytes")
+    torch.cuda.synchronize()
 
+
+# -------------------------------------------------------------------- main
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the causal prefill")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the long decode and the mixed batch")
     ap.add_argument("--extra", action="store_true",
-                    help="also time workloads 3 and 5 and a verification batch (adds ~2 min)")
+                    help="also time the split-KV pair, verification, append and graph batches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--mode", choices=["bench", "traffic"], default="bench")
     ap.add_argument("--decode-plan", choices=["balanced", "chunked"], default="balanced",
                     help="decode kernels to time (default: the automatic plan's, balanced)")
@@ -431,23 +619,40 @@ def main():
         return
 
     log("[bench] decode workload: generating inputs")
-    dec = bench_decode(args, torch, sa, device, W)
-    log(f"[bench] decode: {dec['ms_step']:.4f} ms/step, kernel {dec['kern_ms']:.4f} ms")
+    b = W.config(2)
+    balanced = args.decode_plan == "balanced"
+    dec = time_decode(torch, sa, device, b, args.steps, args.warmup, balanced=balanced,
+                      kv_copies=KV_COPIES, event_every=EVENT_EVERY)
+    log(f"[bench] decode: {dec['ms_step']:.4f} ms/step, first pass {dec['kern_ms']:.4f} ms")
+    plan = dec["plan"]
+    del dec["db"], dec["ks"], dec["vs"], dec["first"]
+    torch.cuda.empty_cache()
     pre = None
     if not args.no_prefill:
         log("[bench] prefill workload: generating inputs")
-        pre = bench_prefill(args, torch, sa, device, W)
+        b4 = W.config(4)
+        _, ms = time_prefill(torch, device, b4, max(5, min(args.steps, 20)), args.warmup)
+        pre = prefill_entry(W.CONFIG_NAMES[4], b4, ms, max(5, min(args.steps, 20)),
+                            traffic=traffic_of("prefill"))
         log(f"[bench] prefill: {pre['ms_per_call']} ms, {pre['value']} TFLOP/s")
+        del b4
+        torch.cuda.empty_cache()
+    wl = None
+    if not args.no_workloads:
+        wl = bench_workloads(args, torch, sa, device, W)
+        for k, v in wl.items():
+            if "roofline" in v:
+                log(f"[bench] {k}: {v['ms_per_call']} ms, roofline frac {v['roofline']['frac']}")
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        cpu = cpu_baseline(dec["batch"], dec["kv_bytes"], args.cpu_seconds)
+        cpu = cpu_baseline(W, b, args.cpu_seconds)
 
-    b = dec["batch"]
     achieved = dec["alg_bytes"] / (dec["kern_ms"] * 1e-3) / 1e9
+    whole = dec["alg_bytes"] / (dec["ms_step"] * 1e-3) / 1e9
     line = {
         "metric": "sink-GQA prefill TFLOP/s and decode KV GB/s at 1 MI355X, % of roofline",
-        "value": round(dec["value"], 2),
+        "value": round(dec["kv_bytes"] / (dec["ms_step"] * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -462,16 +667,16 @@ def main():
             "workload": W.CONFIG_NAMES[2],
             "batch": b.batch, "kv_tokens": int(b.kv_len.sum()), "num_qo_heads": b.num_qo_heads,
             "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "page_size": b.page_size,
-            **dec["plan"], "kv_copies_rotated": KV_COPIES, "out_dtype": "f32",
+            **plan, "kv_copies_rotated": KV_COPIES, "out_dtype": "f32",
             "step": ("sink_attn_decode_balanced_partial + sink_attn_decode_balanced_finish"
-                     if args.decode_plan == "balanced"
-                     else "sink_attn_decode_partial + sink_attn_merge"),
+                     if balanced else "sink_attn_decode_partial + sink_attn_merge"),
+            "whole_step_frac_hbm": round(whole / HBM_PEAK_GBS, 4),
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": DECODE_TRAFFIC_BYTES if args.decode_plan == "balanced" else None,
-            "kernel": ("decode_balanced_kernel<8> (first pass)" if args.decode_plan == "balanced"
+            "traffic": traffic_of("decode_balanced") if balanced else None,
+            "kernel": ("decode_balanced_kernel<8> (first pass)" if balanced
                        else "decode_kernel<8> (split-KV partial)"),
             "kernel_ms": round(dec["kern_ms"], 5), "kernel_samples": dec["kern_samples"],
             "algorithmic_bytes": dec["alg_bytes"],
@@ -480,6 +685,8 @@ def main():
     }
     if pre is not None:
         line["prefill"] = pre
+    if wl is not None:
+        line["workloads"] = wl
     if args.extra:
         line["extra"] = bench_extra(args, torch, sa, device, W)
     print(json.dumps(line), flush=True)

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "launch.hpp"
 
@@ -35,15 +36,41 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 constexpr int kHeadDim = 64;
 constexpr int kPageSize = 16;
 
-sink_attn_status check_heads(int32_t hq, int32_t hkv, bool decode) {
+sink_attn_status check_heads(int32_t hq, int32_t hkv) {
   if (hq <= 0 || hkv <= 0) return fail(SINK_ATTN_ERR_BAD_SHAPE, "head counts must be positive (Hq=%d, Hkv=%d)", hq, hkv);
   if (hq % hkv) return fail(SINK_ATTN_ERR_BAD_SHAPE, "Hq=%d is not a multiple of Hkv=%d", hq, hkv);
   const int G = hq / hkv;
-  const bool supported = G == 1 || G == 2 || G == 4 || G == 8 || (decode && G == 16);
-  if (!supported)
-    return fail(SINK_ATTN_ERR_UNSUPPORTED, "group size Hq/Hkv=%d is not built (%s)", G,
-                decode ? "decode supports 1, 2, 4, 8, 16" : "prefill supports 1, 2, 4, 8");
+  if (!(G == 1 || G == 2 || G == 4 || G == 8 || G == 16))
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "group size Hq/Hkv=%d is not built (1, 2, 4, 8, 16)", G);
   return ok();
+}
+
+// Compute units of the current device, queried once per device.  The
+// automatic plans size their grids to the machine (one workgroup per CU for
+// the balanced decode, a few per CU elsewhere), so a device that exposes
+// fewer CUs (a partitioned GPU) gets a grid that still divides evenly.
+// Without a usable device (host-only planning, no GPU) the full MI355X's 256.
+constexpr int kDefaultCUs = 256;
+constexpr int kMaxDevices = 64;
+std::once_flag g_cu_once[kMaxDevices];
+int g_cu_count[kMaxDevices];
+
+int device_cus() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();  // leave no sticky error for the next launch check
+    return kDefaultCUs;
+  }
+  std::call_once(g_cu_once[dev], [dev]() {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+      (void)hipGetLastError();
+      n = kDefaultCUs;
+    }
+    g_cu_count[dev] = n;
+  });
+  return g_cu_count[dev];
 }
 
 sink_attn_status hip_status(hipError_t e, const char* what) {
@@ -52,7 +79,7 @@ sink_attn_status hip_status(hipError_t e, const char* what) {
 }
 
 // Keys per split are rounded to whole pages.  The automatic plan aims at
-// several waves per compute unit across 256 CUs while keeping each split at
+// eight workgroups (32 waves) per compute unit while keeping each split at
 // least 16 pages long, so that a workgroup amortises its merge.
 int32_t plan_splits(int32_t batch, int32_t hkv, int32_t max_kv_len, int32_t requested) {
   const int32_t pages = (max_kv_len + kPageSize - 1) / kPageSize;
@@ -63,7 +90,7 @@ int32_t plan_splits(int32_t batch, int32_t hkv, int32_t max_kv_len, int32_t requ
   }
   if (pages <= 16) return 1;
   const int64_t units = (int64_t)batch * hkv;
-  const int64_t target_wgs = 2048;  // 8 workgroups (32 waves) per CU on 256 CUs
+  const int64_t target_wgs = 8 * (int64_t)device_cus();
   int64_t s = (target_wgs + units - 1) / units;
   const int64_t max_by_len = (pages + 15) / 16;  // >= 16 pages per split
   if (s > max_by_len) s = max_by_len;
@@ -76,21 +103,14 @@ int32_t plan_splits(int32_t batch, int32_t hkv, int32_t max_kv_len, int32_t requ
 // equal ranges (a multiple of 4: one workgroup holds four ranges, one per
 // wave).  Every range carries the same work, so the grid must spread evenly
 // over the compute units: the automatic plan launches at most one workgroup
-// per CU (kTargetWorkgroups), i.e. one streaming wave per SIMD, which keeps
-// two K/V steps in flight per wave -- enough to saturate HBM -- and makes
-// the ranges as long as possible, so the start-up of a wave and the merge of
-// a request's partials stay small against its streaming.  Ranges shorter
-// than kMinRangePages pages are not worth a wave.  An explicit request takes
-// exactly that many ranges (rounded up to a multiple of 4) and allows ranges
-// down to one page.
-#ifndef SA_TARGET_WORKGROUPS
-#define SA_TARGET_WORKGROUPS 256
-#endif
-#ifndef SA_MIN_RANGE_PAGES
-#define SA_MIN_RANGE_PAGES 8
-#endif
-constexpr int64_t kTargetWorkgroups = SA_TARGET_WORKGROUPS;
-constexpr int32_t kMinRangePages = SA_MIN_RANGE_PAGES;
+// per CU (the device's CU count), i.e. one streaming wave per SIMD, which
+// keeps two K/V steps in flight per wave -- enough to saturate HBM -- and
+// makes the ranges as long as possible, so the start-up of a wave and the
+// merge of a request's partials stay small against its streaming.  Ranges
+// shorter than kMinRangePages pages are not worth a wave.  An explicit request
+// takes exactly that many ranges (rounded up to a multiple of 4) and allows
+// ranges down to one page.
+constexpr int32_t kMinRangePages = 8;
 constexpr int32_t kMaxRanges = 1 << 20;
 
 struct RangePlan {
@@ -106,7 +126,7 @@ RangePlan plan_ranges(int32_t batch, int32_t hkv, int32_t max_kv_len, int32_t re
     min_pages = 1;
   } else {
     const int64_t pages_ub = (int64_t)batch * ((max_kv_len + kPageSize - 1) / kPageSize);
-    const int64_t wgs_per_head = kTargetWorkgroups / hkv;
+    const int64_t wgs_per_head = device_cus() / hkv;
     r = 4 * (wgs_per_head > 1 ? wgs_per_head : 1);
     const int64_t by_len = (pages_ub + kMinRangePages - 1) / kMinRangePages;
     if (r > by_len) r = (by_len + 3) / 4 * 4;
@@ -213,7 +233,7 @@ sink_attn_status sink_attn_prefill(const void* q, const int32_t* qo_indptr, cons
     return fail(SINK_ATTN_ERR_BAD_SHAPE, "prefill: max_qlen=%d exceeds total_q=%d", max_qlen, total_q);
   if (causal && max_qlen > 0 && max_kv_len <= 0)
     return fail(SINK_ATTN_ERR_BAD_SHAPE, "prefill: causal queries need keys (max_kv_len=%d)", max_kv_len);
-  sink_attn_status st = check_heads(num_qo_heads, num_kv_heads, false);
+  sink_attn_status st = check_heads(num_qo_heads, num_kv_heads);
   if (st != SINK_ATTN_OK) return st;
   if (head_dim != kHeadDim)
     return fail(SINK_ATTN_ERR_UNSUPPORTED, "prefill: head_dim=%d (only 64 is built)", head_dim);
@@ -305,7 +325,7 @@ sink_attn_status check_decode_common(const void* q, const void* k_pages, const v
   if (batch <= 0 || max_kv_len < 0 || num_splits < 0)
     return fail(SINK_ATTN_ERR_BAD_SHAPE, "decode: batch=%d max_kv_len=%d num_splits=%d", batch,
                 max_kv_len, num_splits);
-  sink_attn_status st = check_heads(num_qo_heads, num_kv_heads, true);
+  sink_attn_status st = check_heads(num_qo_heads, num_kv_heads);
   if (st != SINK_ATTN_OK) return st;
   if (head_dim != kHeadDim)
     return fail(SINK_ATTN_ERR_UNSUPPORTED, "decode: head_dim=%d (only 64 is built)", head_dim);
@@ -463,7 +483,7 @@ sink_attn_status balanced_setup(const void* q, const void* k_pages, const void* 
     if (!page_indptr) return fail(SINK_ATTN_ERR_NULL_ARG, "%s: page_indptr is required", who);
     if (batch <= 0 || max_kv_len < 0)
       return fail(SINK_ATTN_ERR_BAD_SHAPE, "%s: batch=%d max_kv_len=%d", who, batch, max_kv_len);
-    sink_attn_status st = check_heads(num_qo_heads, num_kv_heads, true);
+    sink_attn_status st = check_heads(num_qo_heads, num_kv_heads);
     if (st != SINK_ATTN_OK) return st;
     if (head_dim != kHeadDim)
       return fail(SINK_ATTN_ERR_UNSUPPORTED, "%s: head_dim=%d (only 64 is built)", who, head_dim);
@@ -587,11 +607,10 @@ int32_t verify_column_groups(int32_t columns) {
 // Split plan of the verification kernel.  Each chunk of a request re-reads
 // its queries, merges its four waves and writes partials that a second
 // kernel merges, so splitting only pays when the grid would not fill the
-// GPU: one chunk while batch x Hkv x column groups reaches half of
-// kVerifyTargetWorkgroups (two workgroups per CU), else enough chunks to
-// reach it, each of at least 16 pages.  An explicit request is taken as
-// sink_attn_decode takes it.
-constexpr int64_t kVerifyTargetWorkgroups = 512;
+// GPU: one chunk while batch x Hkv x column groups reaches one workgroup
+// per CU, else enough chunks for two workgroups per CU, each of at least 16
+// pages.  An explicit request is taken as sink_attn_decode takes it.
+int64_t verify_target_workgroups() { return 2 * (int64_t)device_cus(); }
 
 // Wide drafts, more than kVerifyTileMinColumns (token, head) pairs per KV
 // head, run the tile kernel (verify_tile.hip): 128-row tiles on 32x32 MFMAs
@@ -603,15 +622,15 @@ constexpr int32_t kVerifyTileRows = 128;
 constexpr int32_t kVerifyTileKeys = 64;
 constexpr int32_t kVerifyTileMaxChunks = 64;
 // Automatic chunking of the tile kernel: enough chunks of at least 8 tiles
-// (512 keys) for about kVerifyTileTargetItems (request, KV head, chunk)
-// items if every request had max_kv_len keys; each item runs one workgroup
+// (512 keys) for about four (request, KV head, chunk) items per CU
+// if every request had max_kv_len keys; each item runs one workgroup
 // per 128-row tile.  One item per (request, KV head) lets the longest
 // requests bound a ragged batch; chunks cut them at the price of partial
 // writes and a merge pass.  Measured on 64 requests (L <= 4,096, 512
 // (request, KV head) pairs): 16-token drafts 0.089 ms in one chunk, 0.077
 // in two, 0.080 in three; 32-token trees (two row tiles) 0.144, 0.136 and
 // 0.139 -- two chunks in both, whatever the row tiles.
-constexpr int64_t kVerifyTileTargetItems = 1024;
+int64_t verify_tile_target_items() { return 4 * (int64_t)device_cus(); }
 constexpr int32_t kVerifyTileMinChunkTiles = 8;
 
 bool verify_uses_tiles(int32_t group, int32_t columns) {
@@ -633,7 +652,8 @@ TilePlan verify_tile_plan(int32_t batch, int32_t hkv, int32_t columns, int32_t m
     want = requested;
   } else {
     const int64_t pairs = (int64_t)batch * hkv;
-    want = pairs > 0 ? (kVerifyTileTargetItems + pairs - 1) / pairs : 1;
+    const int64_t target = verify_tile_target_items();
+    want = pairs > 0 ? (target + pairs - 1) / pairs : 1;
     const int64_t by_len = tiles / kVerifyTileMinChunkTiles;
     if (want > by_len) want = by_len;
   }
@@ -654,8 +674,9 @@ int32_t verify_plan_splits(int32_t batch, int32_t hkv, int32_t columns, int32_t 
   if (requested > 0) return plan_splits(batch, hkv, max_kv_len, requested);
   const int32_t pages = (max_kv_len + kPageSize - 1) / kPageSize;
   const int64_t units = (int64_t)batch * hkv * verify_column_groups(columns);
-  if (units <= 0 || units * 2 >= kVerifyTargetWorkgroups || pages <= 16) return 1;
-  int64_t s = (kVerifyTargetWorkgroups + units - 1) / units;
+  const int64_t target = verify_target_workgroups();
+  if (units <= 0 || units * 2 >= target || pages <= 16) return 1;
+  int64_t s = (target + units - 1) / units;
   const int64_t max_by_len = (pages + 15) / 16;
   if (s > max_by_len) s = max_by_len;
   if (s > 256) s = 256;

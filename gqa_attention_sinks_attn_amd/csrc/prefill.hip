@@ -8,9 +8,10 @@
 //
 // Work decomposition (one workgroup = 4 waves = 256 packed query rows):
 //   * rows are (token, query head) pairs of ONE KV head g: 32-row column
-//     blocks, each one head x 32 consecutive tokens; eight blocks per
-//     workgroup, so a workgroup covers 256 / G tokens x G heads and every
-//     K/V tile it stages in LDS is reused by all 256 rows (GQA packing);
+//     blocks, each one head x 32 consecutive tokens (two heads x 16 tokens
+//     when G = 16); eight blocks per workgroup, so a workgroup covers
+//     256 / G tokens x G heads and every K/V tile it stages in LDS is reused
+//     by all 256 rows (GQA packing);
 //   * keys are walked in tiles of 64 up to the causal edge of the
 //     workgroup's last token; K and V tiles go straight from global memory
 //     into LDS (three buffers: the next two tiles are in flight while one
@@ -97,11 +98,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int cbi = 2 * wave + cb;
-    head[cb] = g * G + (cbi % G);
-    tok[cb] = t0 + 32 * (cbi / G) + r;
+    // Row map of column block cbi: with 32 or more tokens per workgroup
+    // (G <= 8) a block is 32 consecutive tokens of one head; with 16 (G = 16)
+    // it is two heads x 16 tokens (workgroup row 32 cbi + r is head
+    // (32 cbi + r) / 16, token r % 16).
+    int hl, tl, tl_last;
+    if constexpr (T >= 32) {
+      hl = cbi % G;
+      tl = 32 * (cbi / G) + r;
+      tl_last = 32 * (cbi / G) + 31;
+    } else {
+      hl = (32 * cbi + r) / T;
+      tl = r % T;
+      tl_last = T - 1;
+    }
+    head[cb] = g * G + hl;
+    tok[cb] = t0 + tl;
     valid[cb] = tok[cb] < qlen;
     pos[cb] = valid[cb] ? pos_base + tok[cb] : -1;
-    const int last_tok = min(t0 + 32 * (cbi / G) + 31, qlen - 1);
+    const int last_tok = min(t0 + tl_last, qlen - 1);
     wave_pos_max = max(wave_pos_max, pos_base + last_tok);
     const uint16_t* qrow =
         p.q + ((int64_t)(q_begin + (valid[cb] ? tok[cb] : 0)) * p.hq + head[cb]) * kD + 8 * hh;
@@ -461,6 +476,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t stream) {
     case 2: return launch_g<2>(a, stream);
     case 4: return launch_g<4>(a, stream);
     case 8: return launch_g<8>(a, stream);
+    case 16: return launch_g<16>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

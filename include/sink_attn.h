@@ -24,13 +24,18 @@
  *     the call returns without synchronising.  The caller owns every buffer
  *     and keeps inputs alive until the stream's work completes.
  *   - The library allocates no device memory, keeps no pointer after
- *     returning and holds no state other than a thread-local error string,
- *     so calls from several host threads are safe.
+ *     returning and holds no state other than a thread-local error string
+ *     and the per-device compute-unit count (written once, under
+ *     std::call_once), so calls from several host threads are safe.
  *   - bf16 tensors are raw bfloat16 bit patterns; all of q, k, v, out and a
  *     workspace must be 16-byte aligned; int32 index arrays 4-byte aligned.
  *   - head_dim must be 64 and page_size 16 (SINK_ATTN_ERR_UNSUPPORTED
- *     otherwise).  Hq must be a multiple of Hkv; prefill supports
- *     Hq / Hkv in {1, 2, 4, 8}, decode Hq / Hkv in {1, 2, 4, 8, 16}.
+ *     otherwise).  Hq must be a multiple of Hkv, with Hq / Hkv in
+ *     {1, 2, 4, 8, 16} for every entry point.
+ *   - Automatic plans size their grids from the current device's compute
+ *     unit count, queried once per device (256, a whole MI355X, when no
+ *     device can be queried); the host-only planning queries below use the
+ *     same count, so they agree with the launches on the same device.
  *   - sinks: fp32 [Hq] in logit units (not multiplied by sm_scale); NULL
  *     means no sink (sigma = -inf), i.e. standard attention.  A sink of
  *     +inf gives o = 0, lse = +inf.
@@ -116,7 +121,7 @@ sink_attn_status sink_attn_prefill(
 /*
  * Number of KV chunks per request of the split-KV plan for these sizes
  * (num_splits = 0: the planner's choice, as sink_attn_decode_partial uses
- * it; always >= 1).  Host-only; no device access.
+ * it; always >= 1).  Host-only: no launch, no copy.
  */
 int32_t sink_attn_decode_num_splits(int32_t batch, int32_t num_qo_heads,
                                     int32_t num_kv_heads, int32_t max_kv_len,
@@ -124,7 +129,9 @@ int32_t sink_attn_decode_num_splits(int32_t batch, int32_t num_qo_heads,
 
 /*
  * Workspace bytes that sink_attn_decode needs for these sizes and
- * num_splits.  num_splits = 0 (the automatic plan): when max_kv_len exceeds
+ * num_splits.  Takes num_kv_heads and max_kv_len besides the batch, head
+ * and split counts because the automatic plan picks the load-balanced
+ * workspace (sized by its page ranges per KV head) from them.  num_splits = 0 (the automatic plan): when max_kv_len exceeds
  * 16 pages the call runs the load-balanced plan and needs
  * sink_attn_decode_balanced_workspace_size(..., num_ranges = 0) bytes;
  * otherwise one chunk per request and 0 bytes.  num_splits = S > 0: 0 when
@@ -347,8 +354,8 @@ size_t sink_attn_verify_workspace_size(int32_t batch, int32_t num_qo_heads,
 
 /*
  * The chunk count S that sink_attn_verify and sink_attn_verify_tree use for
- * these sizes (num_splits = 0: the automatic plan above).  Host-only; 1 for
- * invalid sizes.
+ * these sizes (num_splits = 0: the automatic plan above).  Host-only (no
+ * launch, no copy); 1 for invalid sizes.
  */
 int32_t sink_attn_verify_num_splits(int32_t batch, int32_t num_qo_heads,
                                     int32_t num_kv_heads, int32_t max_qlen,

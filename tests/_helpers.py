@@ -5,6 +5,10 @@ import numpy as np
 
 from workloads import Batch, to_bf16_bits
 
+# (case name, elements compared, max-abs error, relative L2 error) of every
+# parity check of the session, for the terminal summary.
+PARITY_RECORD: list = []
+
 
 def batch_from_values(q, k, v, *, qlens, kv_lens, hq, hkv, d, sinks, sm_scale, causal,
                       kind="prefill") -> Batch:

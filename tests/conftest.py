@@ -16,3 +16,15 @@ def pytest_configure(config):
         _b.build()
     import oracle
     oracle.build(force=False)
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Parity of the five workloads (whole tensors where compared whole), so
+    that the figures appear in the run's output even under -q."""
+    from tests._helpers import PARITY_RECORD
+    rows = [r for r in PARITY_RECORD if r[0].split()[0] in ("c1", "c2", "c3", "c4", "c5")]
+    if not rows:
+        return
+    terminalreporter.write_line("parity against the fp64 oracle (max-abs <= 1e-2, rel-L2 <= 5e-3):")
+    for name, n, mx, rl in rows:
+        terminalreporter.write_line(f"  {name}: {n} values, max_abs={mx:.3e}, rel_l2={rl:.3e}")

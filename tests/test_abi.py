@@ -70,7 +70,7 @@ def call_prefill(**over):
     (dict(num_kv_heads=7), SHAPE), (dict(num_qo_heads=0), SHAPE), (dict(sm_scale=0.0), SHAPE),
     (dict(sm_scale=float("inf")), SHAPE), (dict(max_kv_len=0), SHAPE),
     (dict(head_dim=128), UNSUP), (dict(page_indices=A, kv_len=A, page_size=32), UNSUP),
-    (dict(num_qo_heads=128, num_kv_heads=8), UNSUP), (dict(num_qo_heads=24, num_kv_heads=8), UNSUP),
+    (dict(num_qo_heads=256, num_kv_heads=8), UNSUP), (dict(num_qo_heads=24, num_kv_heads=8), UNSUP),
     (dict(out_dtype=7), UNSUP),
     (dict(q=A + 2), MISAL), (dict(k=A + 8), MISAL), (dict(out=A2 + 4), MISAL),
     (dict(qo_indptr=A + 1), MISAL), (dict(lse=A3 + 2), MISAL),

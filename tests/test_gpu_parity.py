@@ -15,6 +15,8 @@ Each test names its case; everything calls the library through the C ABI
 """
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 import pytest
 
@@ -23,7 +25,11 @@ pytestmark = pytest.mark.gpu
 
 import oracle  # noqa: E402
 import workloads as W  # noqa: E402
-from tests._helpers import rel_l2  # noqa: E402
+from tests._helpers import PARITY_RECORD, rel_l2  # noqa: E402
+
+# The two largest workloads are drawn once and shared by their sampled and
+# whole-tensor tests (one at a time: workload 5's page pool is ~4.5 GB).
+config = functools.lru_cache(maxsize=1)(W.config)
 
 MAX_ABS = 1e-2
 REL_L2 = 5e-3
@@ -62,6 +68,7 @@ def check(name, out, ref, lse=None, ref_lse=None, bf16_out=None):
     mx = float(err.max()) if err.size else 0.0
     rl = rel_l2(out, ref)
     print(f"[{name}] max_abs={mx:.3e} rel_l2={rl:.3e} bf16_out={bf16_out}", flush=True)
+    PARITY_RECORD.append((name, out.size, mx, rl))
     allowed = MAX_ABS + (BF16_U * np.abs(ref) if bf16_out else 0.0)
     assert np.all(err <= allowed), f"{name}: max abs {mx} (worst excess {float((err - allowed).max())})"
     if np.linalg.norm(ref) > 1e-6:
@@ -111,7 +118,7 @@ def _sample_rows(b, n, seed):
 
 
 def test_c4_causal_prefill_sampled():
-    b = W.config(4)
+    b = config(4)
     out, lse = gpu_run(b)
     rows, heads = _sample_rows(b, 3000, 4)
     ref, rl = oracle.attend_rows(b, rows, heads)
@@ -122,7 +129,7 @@ def test_c4_causal_prefill_sampled():
 
 
 def test_c5_mixed_full_size_sampled():
-    mx = W.config(5)
+    mx = config(5)
     for part, n, seed in [(mx.prefill, 3000, 51), (mx.decode, 3000, 52)]:
         out, lse = gpu_run(part)
         rows, heads = _sample_rows(part, n, seed)
@@ -132,6 +139,27 @@ def test_c5_mixed_full_size_sampled():
         heads = np.concatenate([heads, np.tile(ex, 8)])
         ref, rl = oracle.attend_rows(part, rows, heads)
         check(f"c5 {part.kind}", out[rows, heads], ref, lse[rows, heads], rl)
+
+
+# Whole-tensor parity of the two largest workloads: every (row, head) of the
+# output against the oracle, max-abs and relative L2 over the whole tensor.
+# The oracle takes about a minute per call on 16 host cores.
+
+@pytest.mark.timeout(1500)
+def test_c4_causal_prefill_whole_tensor():
+    b = config(4)
+    out, lse = gpu_run(b)
+    ref, rl = oracle.attend(b)
+    check("c4 whole tensor", out, ref, lse, rl)
+
+
+@pytest.mark.timeout(1500)
+@pytest.mark.parametrize("part", ["prefill", "decode"])
+def test_c5_mixed_whole_tensor(part):
+    b = getattr(config(5), part)
+    out, lse = gpu_run(b)
+    ref, rl = oracle.attend(b)
+    check(f"c5 {part} whole tensor", out, ref, lse, rl)
 
 
 # ------------------------------------------------------------------- edge cases
@@ -183,7 +211,7 @@ def test_infinite_sink():
         check(f"{kind} +inf sink others", out[:, keep], ref[:, keep], lse[:, keep], rl[:, keep])
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 1), (8, 4), (8, 8), (64, 8), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(4, 1), (8, 4), (8, 8), (64, 8), (16, 2), (64, 4), (16, 1)])
 @pytest.mark.parametrize("paged", [False, True])
 def test_prefill_group_sizes_and_layouts(hq, hkv, paged):
     b = W.make_batch(11 + hq, kind="prefill", qlens=[1, 31, 32, 33, 130], kv_lens=[1, 31, 40, 200, 130],
