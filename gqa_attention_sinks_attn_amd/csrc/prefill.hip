@@ -21,17 +21,18 @@
 //     and the row maximum needs one cross-lane exchange;
 //   * the running maximum is a reference value m: scores are exponentiated
 //     as exp2(s * scale - m) with one FMA and no per-tile maximum; only when
-//     a row's tile sum would exceed 2^15 (a new, much larger maximum) or the
+//     a row's tile sum would exceed 2^16 (a new, much larger maximum) or the
 //     row has no reference yet does the tile take the slow path that finds
 //     the true maximum and rescales m, d and O -- the same quantity as the
 //     textbook update, with the max reduction and the rescale of O skipped
 //     on almost every tile;
 //   * P is rounded to bf16 in registers and fed directly as the B operand of
-//     O^T += V^T P^T; the row sum d adds exactly those rounded values, so the
-//     weights of every row sum to one; V stays in its natural layout in LDS
-//     and is read
-//     transposed with ds_read_b64_tr_b16 in the key order of the score
-//     layout;
+//     O^T += V^T P^T; the row sums of the same rounded values are taken on
+//     the matrix core too (v_mfma_f32_16x16x32_bf16 with a 0/1 A operand),
+//     so the weights of every row sum to one and the vector unit, the
+//     loop's bottleneck, only exponentiates and packs; V stays in its
+//     natural layout in LDS and is read transposed with ds_read_b64_tr_b16
+//     in the key order of the score layout;
 //   * masking (causal edge, ragged tail) is applied only on tiles that
 //     straddle an edge, comparing key offsets inside the tile (constants)
 //     against one per-row limit;
@@ -49,13 +50,7 @@ constexpr int kD = 64;
 constexpr int kTile = 64;            // keys per tile
 constexpr int kTileBytes = kTile * kD * 2;  // one K or V tile in LDS, rows unpadded
 constexpr int kBufs = 3;                    // LDS tile buffers
-constexpr float kFastLimit = 32768.f; // lane-partial tile sum that forces a rescale
-
-// acc + lo(w) + hi(w) for a packed bf16 pair, accumulated in fp32.
-__device__ __forceinline__ float dot2_sum(uint32_t w, float acc) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
-}
+constexpr float kFastLimit = 65536.f; // row tile sum that forces a rescale
 
 template <int G, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs p) {
@@ -132,8 +127,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int kv_hi = p.causal ? min(L, pos_max_wg + 1) : L;
   const int n_tiles = (kv_hi + kTile - 1) / kTile;
 
-  // ---- online state (log2 units); the sink starts every row ----
+  // ---- online state (log2 units); the sink starts every row.  d holds the
+  // sink's term of the denominator (lanes hh = 0); the keys' terms are summed
+  // on the matrix core into dk: in every lane l, element 0 (and 2) holds row
+  // l % 16 of the column block and element 1 (and 3) row 16 + l % 16, so a
+  // lane's own row r = l % 32 is element r / 16 of its own dk. ----
   float m[2], d[2];
+  f32x4 dk[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   f32x16 o[2][2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -253,6 +253,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // block db (chunk 2 (q % 2) + (lane % 4) / 2 + 4 db) and key row
   // 4 hh + (lane % 16) / 4 (+ 8 for the upper four values) of the 16-key
   // slice hf of key block kb, at vread + 4096 kb + 2048 hf + 256 db (+ 1024).
+  // Row sums of P on the matrix core: D(16x16) += A(16x32) B(32x16) with B =
+  // a P^T operand of the O^T product as it stands in registers.  Read as a
+  // 16x16x32 operand, lane l's eight keys are k-group l / 16 of column l % 16,
+  // and they belong to row l % 32 of the column block: k-groups 0 and 2 of
+  // column n are row n, k-groups 1 and 3 row 16 + n.  So the even rows of A
+  // are ones on k-groups 0 and 2 and the odd rows ones on 1 and 3: D[m][n]
+  // is the slice's sum of row n (m even) or row 16 + n (m odd), and lane l,
+  // which holds D rows 4 (l / 16) .. + 3 of column l % 16, gets both.  The
+  // sums add the bf16-rounded weights the O^T product consumes (exact
+  // products, fp32 accumulation), so every row stays an exact convex
+  // combination of V.
+  bf16x8 ones_sel;
+  {
+    const bool one = (((lane & 15) + (lane >> 4)) & 1) == 0;
+    const uint32_t w = one ? 0x3F803F80u : 0u;   // two bf16 1.0 or two zeros
+    ones_sel = as_bf16x8(u32x4{w, w, w, w});
+  }
   const int kread = ((lane & 31) >> 3) * 1024 + 16 * ((2 * (lane & 7) + hh + ((lane >> 3) & 1)) & 15);
   const int vread = 512 * hh + 64 * ((lane & 15) >> 2) + 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) +
                     8 * (lane & 1);
@@ -312,28 +329,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (32 * kb + 8 * (j >> 2) + (j & 3) > rel) sacc[kb][cb][j] = -INFINITY;
       };
       // exp2(s * scale - m) of the scores j = 8 hf + 2 q, +1 (q = 2 qp, 2 qp + 1)
-      // of key block kb, packed; the row sum adds the rounded values the MFMA
-      // consumes (v_dot2 with 1.0 accumulates in fp32), so every row stays an
-      // exact convex combination of V.
-      auto expo4 = [&](int cb, float neg_m, int kb, int hf, int qp, float& acc) {
+      // of key block kb, packed to bf16 (the P^T operand of O^T and of the
+      // row sums).
+      auto expo4 = [&](int cb, float neg_m, int kb, int hf, int qp) {
 #pragma unroll
         for (int q = 2 * qp; q < 2 * qp + 2; ++q) {
           const int j = 8 * hf + 2 * q;
           const float e0 = fast_exp2(__builtin_fmaf(sacc[kb][cb][j], sl2, neg_m));
           const float e1 = fast_exp2(__builtin_fmaf(sacc[kb][cb][j + 1], sl2, neg_m));
-          const uint32_t w = pack_bf16x2(e0, e1);
-          pk[cb][kb][hf][q] = w;
-          acc = dot2_sum(w, acc);
+          pk[cb][kb][hf][q] = pack_bf16x2(e0, e1);
         }
       };
       auto neg_ref = [&](int cb) { return (m[cb] == -INFINITY) ? 0.f : -m[cb]; };
+      auto pb_of = [&](int cb, int kb, int hf) {
+        return as_bf16x8(u32x4{pk[cb][kb][hf][0], pk[cb][kb][hf][1], pk[cb][kb][hf][2], pk[cb][kb][hf][3]});
+      };
+      // Row sums of block cb's tile (layout of dk) from its four P^T operands.
+      auto row_sums = [&](int cb) {
+        f32x4 rs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rs = mfma16(ones_sel, pb_of(cb, i >> 1, i & 1), rs);
+        return rs;
+      };
       // Fast path: the tile was exponentiated against the current reference
-      // m.  It is valid while every p stays below 2^15 and the row has a
-      // reference; otherwise (rare: a new maximum, or the row's first live
-      // tile without a sink) take the true row maximum, rescale O, d and m,
-      // and exponentiate again.
-      auto settle_row = [&](int cb, float ds) {
-        if (__any(!(ds <= kFastLimit) || m[cb] == -INFINITY)) {
+      // m.  It is valid while every row's tile sum stays below 2^16 and the
+      // row has a reference; otherwise (rare: a new maximum, or the row's
+      // first live tile without a sink) take the true row maximum, rescale O,
+      // d, the key sums and m, and exponentiate again.
+      // The sums are compared as unsigned bit patterns: an overflowed weight
+      // makes them inf, or NaN where a 0 of the selector meets it inside the
+      // product, and both patterns exceed the limit's (a float compare would
+      // not see the NaN: device code is built without NaN semantics).
+      auto settle_row = [&](int cb, f32x4 rs) {
+        constexpr uint32_t kLimitBits = 0x47800000u;   // 65536.f
+        static_assert(__builtin_bit_cast(uint32_t, kFastLimit) == kLimitBits, "limit bits");
+        if (__any(__builtin_bit_cast(uint32_t, rs[0]) > kLimitBits ||
+                  __builtin_bit_cast(uint32_t, rs[1]) > kLimitBits || m[cb] == -INFINITY)) {
           float mx = -INFINITY;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
@@ -343,19 +374,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           mx = fmaxf(mx, xor_lane(mx, 32));
           const float m_new = fmaxf(m[cb], mx * sl2);
           const float alpha = (m[cb] == m_new) ? 1.f : fast_exp2(m[cb] - m_new);
+          // the key sums of rows l % 16 and 16 + l % 16: one is this lane's
+          // row, the other's factor lives in lane l ^ 16
+          const float alpha_x = xor_lane(alpha, 16);
+          const bool lo_row = r < 16;
           d[cb] *= alpha;
+          dk[cb][0] *= lo_row ? alpha : alpha_x;
+          dk[cb][1] *= lo_row ? alpha_x : alpha;
           o[cb][0] *= alpha;
           o[cb][1] *= alpha;
           m[cb] = m_new;
-          float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) expo4(cb, neg_ref(cb), i >> 2, (i >> 1) & 1, i & 1, (i & 1) ? a1 : a0);
-          ds = a0 + a1;
+          for (int i = 0; i < 8; ++i) expo4(cb, neg_ref(cb), i >> 2, (i >> 1) & 1, i & 1);
+          rs = row_sums(cb);
         }
-        d[cb] += ds;
-      };
-      auto pb_of = [&](int cb, int kb, int hf) {
-        return as_bf16x8(u32x4{pk[cb][kb][hf][0], pk[cb][kb][hf][1], pk[cb][kb][hf][2], pk[cb][kb][hf][3]});
+        dk[cb][0] += rs[0];
+        dk[cb][1] += rs[1];
       };
 
       // (1) S^T of column block 0.  The tile's K operands are read once and
@@ -372,48 +406,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           sacc[kb][0] = mfma32(ko[s][kb], bq[0][s], s == 0 ? zero16 : sacc[kb][0]);
       if (edge) mask(0);
       // (2) S^T of column block 1 on the matrix core while the vector unit
-      //     exponentiates block 0: one MFMA, then six VALU instructions.
+      //     exponentiates block 0; block 0's row sums go to the matrix core
+      //     as each 16-key slice of P is packed.
       {
-        float a0 = 0.f, a1 = 0.f;
         const float nm = neg_ref(0);
+        f32x4 rs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int s = i >> 1, kb = i & 1;
           sacc[kb][1] = mfma32(ko[s][kb], bq[1][s], s == 0 ? zero16 : sacc[kb][1]);
-          expo4(0, nm, i >> 2, (i >> 1) & 1, i & 1, (i & 1) ? a1 : a0);
+          expo4(0, nm, i >> 2, (i >> 1) & 1, i & 1);
+          if (i & 1) rs = mfma16(ones_sel, pb_of(0, i >> 2, (i >> 1) & 1), rs);
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 12; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // VALU
         }
-        settle_row(0, a0 + a1);
+        settle_row(0, rs);
       }
       if (edge) mask(1);
       // (3) O^T of block 0 += V^T P^T on the matrix core while block 1 is
-      //     exponentiated.  The tile's V^T operands are read once, all at
-      //     the start (the first exponentials cover their latency), and
-      //     serve both blocks.
+      //     exponentiated (its row sums follow each packed slice).  The
+      //     tile's V^T operands are read once, all at the start (the first
+      //     exponentials cover their latency), and serve both blocks.
       bf16x8 vo[2][2][2];
       {
-        float a0 = 0.f, a1 = 0.f;
         const float nm = neg_ref(1);
+        f32x4 rs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 8; ++i) vo[i >> 2][(i >> 1) & 1][i & 1] = vop(i >> 2, (i >> 1) & 1, i & 1);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int kb = i >> 2, hf = (i >> 1) & 1, db = i & 1;
           o[0][db] = mfma32(vo[kb][hf][db], pb_of(0, kb, hf), o[0][db]);
-          expo4(1, nm, i >> 2, (i >> 1) & 1, i & 1, (i & 1) ? a1 : a0);
+          expo4(1, nm, i >> 2, (i >> 1) & 1, i & 1);
+          if (i & 1) rs = mfma16(ones_sel, pb_of(1, i >> 2, (i >> 1) & 1), rs);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);    // DS read: all of V^T
-        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);    // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);    // VALU
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 12; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
         }
-        settle_row(1, a0 + a1);
+        settle_row(1, rs);
       }
       // (4) O^T of block 1.
 #pragma unroll
@@ -427,7 +464,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // ---- epilogue: o = O / d, lse = m + log2 d (natural log at the boundary) ----
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    const float dt = d[cb] + xor_lane(d[cb], 32);
+    // this lane's row r = lane % 32: the sink's term from lanes r and r + 32,
+    // the keys' terms from element r / 16 of its own key sums
+    const float dt = d[cb] + xor_lane(d[cb], 32) + (r < 16 ? dk[cb][0] : dk[cb][1]);
     if (!valid[cb]) continue;
     const float inv = dt > 0.f ? 1.f / dt : 0.f;
     const int64_t orow = ((int64_t)(q_begin + tok[cb]) * p.hq + head[cb]) * kD;
