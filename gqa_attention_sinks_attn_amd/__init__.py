@@ -25,7 +25,7 @@ __all__ = [
     "sink_attn_decode_balanced_finish", "sink_attn_decode_balanced_workspace_size",
     "sink_attn_decode_num_ranges", "sink_attn_verify", "sink_attn_verify_workspace_size",
     "sink_attn_verify_tree", "sink_attn_verify_num_splits", "sink_attn_rope_table",
-    "sink_attn_qkv_rope_append",
+    "sink_attn_qkv_rope_append", "sink_attn_decode_noalloc",
     "sink_attn_status_string", "sink_attn_last_error", "sink_attn_version",
     "SYMBOLS",
 ]
@@ -40,7 +40,7 @@ SYMBOLS = (
     "sink_attn_decode_balanced_finish", "sink_attn_decode_balanced_workspace_size",
     "sink_attn_decode_num_ranges", "sink_attn_verify", "sink_attn_verify_workspace_size",
     "sink_attn_verify_tree", "sink_attn_verify_num_splits", "sink_attn_rope_table",
-    "sink_attn_qkv_rope_append",
+    "sink_attn_qkv_rope_append", "sink_attn_decode_noalloc",
     "sink_attn_status_string", "sink_attn_last_error", "sink_attn_version",
 )
 
@@ -74,6 +74,9 @@ def lib():
     L.sink_attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                    ctypes.c_float, _P, ctypes.c_int, _P, _P, ctypes.c_size_t, _P]
     L.sink_attn_decode.restype = ctypes.c_int
+    L.sink_attn_decode_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                           _I, ctypes.c_float, _P, ctypes.c_int, _P, _P]
+    L.sink_attn_decode_noalloc.restype = ctypes.c_int
     L.sink_attn_decode_partial.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                            _I, ctypes.c_float, _P, _P, _P]
     L.sink_attn_decode_partial.restype = ctypes.c_int
@@ -201,6 +204,17 @@ def sink_attn_decode(q, k_pages, v_pages, page_indptr, page_indices, kv_len, sin
         int(head_dim), int(page_size), int(max_kv_len), int(num_splits), float(sm_scale),
         _ptr(out), _dtype_code(out_dtype), _ptr(lse), _ptr(workspace), int(workspace_bytes),
         _stream(stream)))
+
+
+def sink_attn_decode_noalloc(q, k_pages, v_pages, page_indptr, page_indices, kv_len, sinks,
+                             batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                             max_kv_len, num_splits, sm_scale, out, out_dtype, lse,
+                             stream=None) -> None:
+    _check(lib().sink_attn_decode_noalloc(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_indptr), _ptr(page_indices),
+        _ptr(kv_len), _ptr(sinks), int(batch), int(num_qo_heads), int(num_kv_heads),
+        int(head_dim), int(page_size), int(max_kv_len), int(num_splits), float(sm_scale),
+        _ptr(out), _dtype_code(out_dtype), _ptr(lse), _stream(stream)))
 
 
 def sink_attn_decode_partial(q, k_pages, v_pages, page_indptr, page_indices, kv_len, sinks,

@@ -18,8 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsink_attn.so")
-SOURCES = ["api.cpp", "decode.hip", "decode_balanced.hip", "merge.hip", "prefill.hip",
-           "rope_append.hip", "verify.hip", "verify_tile.hip"]
+SOURCES = ["api.cpp", "decode.hip", "decode_balanced.hip", "merge.hip", "noalloc.hip",
+           "prefill.hip", "rope_append.hip", "verify.hip", "verify_tile.hip"]
 ARCH = "gfx950"
 
 

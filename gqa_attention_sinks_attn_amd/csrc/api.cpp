@@ -153,6 +153,12 @@ int32_t chunk_pages_for(int32_t max_kv_len, int32_t splits) {
 
 }  // namespace
 
+namespace sa {
+// Records the failure of an entry point defined in another source file, as
+// the calling thread's last error.
+sink_attn_status api_fail(sink_attn_status s, const char* detail) { return fail(s, "%s", detail); }
+}  // namespace sa
+
 extern "C" {
 
 const char* sink_attn_status_string(sink_attn_status s) {
@@ -398,13 +404,17 @@ sink_attn_status sink_attn_decode_partial(const void* q, const void* k_pages, co
                     "decode_partial launch");
 }
 
-sink_attn_status sink_attn_decode(const void* q, const void* k_pages, const void* v_pages,
-                                  const int32_t* page_indptr, const int32_t* page_indices,
-                                  const int32_t* kv_len, const float* sinks, int32_t batch,
-                                  int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t page_size, int32_t max_kv_len, int32_t num_splits,
-                                  float sm_scale, void* out, sink_attn_dtype out_dtype, float* lse,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace sa {
+// Every host check of sink_attn_decode except the workspace's.
+sink_attn_status decode_arguments_ok(const void* q, const void* k_pages, const void* v_pages,
+                                     const int32_t* page_indptr, const int32_t* page_indices,
+                                     const int32_t* kv_len, const float* sinks, int32_t batch,
+                                     int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t page_size, int32_t max_kv_len, int32_t num_splits,
+                                     float sm_scale, const void* out, sink_attn_dtype out_dtype,
+                                     const float* lse) {
   sink_attn_status st = check_decode_common(q, k_pages, v_pages, page_indptr, page_indices, kv_len,
                                             sinks, batch, num_qo_heads, num_kv_heads, head_dim,
                                             page_size, max_kv_len, num_splits, sm_scale);
@@ -414,6 +424,23 @@ sink_attn_status sink_attn_decode(const void* q, const void* k_pages, const void
     return fail(SINK_ATTN_ERR_UNSUPPORTED, "decode: unknown out_dtype %d", (int)out_dtype);
   if (!aligned(out, 16) || (lse && !aligned(lse, 4)))
     return fail(SINK_ATTN_ERR_MISALIGNED, "decode: out must be 16-byte and lse 4-byte aligned");
+  return ok();
+}
+}  // namespace sa
+
+extern "C" {
+
+sink_attn_status sink_attn_decode(const void* q, const void* k_pages, const void* v_pages,
+                                  const int32_t* page_indptr, const int32_t* page_indices,
+                                  const int32_t* kv_len, const float* sinks, int32_t batch,
+                                  int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t page_size, int32_t max_kv_len, int32_t num_splits,
+                                  float sm_scale, void* out, sink_attn_dtype out_dtype, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  sink_attn_status st = sa::decode_arguments_ok(
+      q, k_pages, v_pages, page_indptr, page_indices, kv_len, sinks, batch, num_qo_heads,
+      num_kv_heads, head_dim, page_size, max_kv_len, num_splits, sm_scale, out, out_dtype, lse);
+  if (st != SINK_ATTN_OK) return st;
 
   if (auto_uses_balanced(max_kv_len, num_splits))
     return sink_attn_decode_balanced(q, k_pages, v_pages, page_indptr, page_indices, kv_len, sinks,

@@ -180,6 +180,37 @@ sink_attn_status sink_attn_decode(
     void* stream);
 
 /*
+ * sink_attn_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same call and result as sink_attn_decode with the same arguments, minus
+ * the workspace, which is taken from a fixed 16 MiB device array of this
+ * library (one per GPU, held from library load until the process ends; its
+ * device address is looked up once per device, on the first call made with
+ * that device current).  Nothing is allocated or freed.
+ *
+ *   Limit: sink_attn_decode_workspace_size() for these arguments must be at
+ *   most 16 MiB (16,777,216 bytes), else SINK_ATTN_ERR_WORKSPACE with nothing
+ *   enqueued (for 64 query heads and the automatic plan, about 880 requests
+ *   of up to 4,096 keys).  Sizes that need no workspace never touch the array.
+ *   Every call on one GPU shares that GPU's array, which keeps the previous
+ *   call's contents; nothing in it needs clearing between calls.  Calls that
+ *   overlap in time on one GPU (other streams, other host threads) race on
+ *   the array: serialise them.
+ */
+sink_attn_status sink_attn_decode_noalloc(
+    const void* q,
+    const void* k_pages, const void* v_pages,
+    const int32_t* page_indptr, const int32_t* page_indices,
+    const int32_t* kv_len,
+    const float* sinks,
+    int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t page_size,
+    int32_t max_kv_len, int32_t num_splits,
+    float sm_scale,
+    void* out, sink_attn_dtype out_dtype, float* lse,
+    void* stream);
+
+/*
  * The first half of sink_attn_decode on its own: the split-KV partial pass,
  * without the merge.  Same arguments and planning as sink_attn_decode
  * (num_splits = 0 -> automatic plan; the plan's S is

@@ -471,3 +471,19 @@ def call_append(**over):
 ])
 def test_qkv_rope_append_validation(over, code):
     assert call_append(**over) == code
+
+
+def test_decode_noalloc_rejects_sizes_beyond_its_array():
+    """The static scratch array holds 16 MiB: larger workspaces are refused on
+    the host, before any device access (fake pointers stay untouched)."""
+    lib = sa.lib()
+    B, Hq, Hkv = 1200, 64, 8
+    need = lib.sink_attn_decode_workspace_size(B, Hq, Hkv, 64, 4096, 0)
+    assert need > 16 << 20
+    rc = lib.sink_attn_decode_noalloc(A, A, A, A, A, A, A, B, Hq, Hkv, 64, 16, 4096, 0, 0.125, A2,
+                                      1, None, None)
+    assert rc == WS
+    assert "static scratch" in sa.sink_attn_last_error()
+    # the usual argument checks still come first for invalid sizes
+    assert lib.sink_attn_decode_noalloc(None, A, A, A, A, A, A, 4, Hq, Hkv, 64, 16, 4096, 0, 0.125,
+                                        A2, 1, None, None) == NULL
