@@ -62,8 +62,11 @@ CSRC = os.path.join(ROOT, "gqa_attention_sinks_attn_amd", "csrc")
 # kernel and by the hash of the sources that build it.  A source change
 # makes the figure stale: it is then reported as null until retaken.
 TRAFFIC = {
-    "decode_balanced": (260_946_607, "decode_balanced.hip", "e0a3f331d123b616"),
-    "prefill": (None, "prefill.hip", ""),
+    "c2": (260_943_357, "decode_balanced.hip", "e0a3f331d123b616"),
+    "c3": (1_076_443_896, "decode_balanced.hip", "e0a3f331d123b616"),
+    "c4": (1_876_166_305, "prefill.hip", "c0e75267ff8df849"),
+    "c5_prefill": (6_378_097_745, "prefill.hip", "c0e75267ff8df849"),
+    "c5_decode": (4_355_372_852, "decode_balanced.hip", "e0a3f331d123b616"),
 }
 
 
@@ -75,8 +78,8 @@ def sources_hash(main: str) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_of(kernel: str):
-    nbytes, main, digest = TRAFFIC[kernel]
+def traffic_of(workload: str):
+    nbytes, main, digest = TRAFFIC[workload]
     if nbytes is None or sources_hash(main) != digest:
         return None
     return nbytes
@@ -251,7 +254,8 @@ def bench_workloads(args, torch, sa, device, W):
     b3 = W.config(3)
     r3 = time_decode(torch, sa, device, b3, steps, warm)
     out["c3_split_decode"] = decode_entry(W.CONFIG_NAMES[3], b3, r3,
-                                          "decode_balanced_kernel<8> (first pass)")
+                                          "decode_balanced_kernel<8> (first pass)",
+                                          traffic=traffic_of("c3"))
     out["c3_split_decode"]["note"] = (
         "the 32 chunks of the workload are the page ranges of the automatic plan; "
         "the split-KV pair with S = 32 is timed under extra")
@@ -262,10 +266,11 @@ def bench_workloads(args, torch, sa, device, W):
     mx = W.config(5)
     pdb, pms = time_prefill(torch, device, mx.prefill, steps, warm)
     out["c5_prefill"] = prefill_entry(W.CONFIG_NAMES[5] + " -- (i) chunked prefills",
-                                      mx.prefill, pms, steps)
+                                      mx.prefill, pms, steps, traffic=traffic_of("c5_prefill"))
     r5 = time_decode(torch, sa, device, mx.decode, steps, warm)
     out["c5_decode"] = decode_entry(W.CONFIG_NAMES[5] + " -- (ii) decodes", mx.decode, r5,
-                                    "decode_balanced_kernel<8> (first pass)")
+                                    "decode_balanced_kernel<8> (first pass)",
+                                    traffic=traffic_of("c5_decode"))
     # both calls back to back on one stream, as one step of the mixed batch
     ddb = r5["db"]
 
@@ -633,7 +638,7 @@ def main():
         b4 = W.config(4)
         _, ms = time_prefill(torch, device, b4, max(5, min(args.steps, 20)), args.warmup)
         pre = prefill_entry(W.CONFIG_NAMES[4], b4, ms, max(5, min(args.steps, 20)),
-                            traffic=traffic_of("prefill"))
+                            traffic=traffic_of("c4"))
         log(f"[bench] prefill: {pre['ms_per_call']} ms, {pre['value']} TFLOP/s")
         del b4
         torch.cuda.empty_cache()
@@ -675,7 +680,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_of("decode_balanced") if balanced else None,
+            "traffic": traffic_of("c2") if balanced else None,
             "kernel": ("decode_balanced_kernel<8> (first pass)" if balanced
                        else "decode_kernel<8> (split-KV partial)"),
             "kernel_ms": round(dec["kern_ms"], 5), "kernel_samples": dec["kern_samples"],
