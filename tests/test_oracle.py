@@ -403,3 +403,15 @@ def test_paged_recipe_structure():
             assert np.all(bf16_bits_to_f32(b.v[last, :, used:]) == 100.0)
     # a rel_l2 sanity check of the helper used by the parity tests
     assert rel_l2(np.ones(4), np.ones(4)) == 0.0
+
+
+def test_planted_mistakes_still_apply():
+    """The planted-mistake list (tests/oracle_mutations.py, run by hand: every
+    mistake must fail a pin) still applies to the current oracle sources."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "oracle_mutations", os.path.join(os.path.dirname(__file__), "oracle_mutations.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod.check_applicable()
+    assert len(mod.MUTATIONS) >= 30
