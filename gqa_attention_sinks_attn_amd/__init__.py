@@ -111,7 +111,7 @@ def lib():
     L.sink_attn_verify_num_splits.argtypes = [_I, _I, _I, _I, _I, _I]
     L.sink_attn_verify_num_splits.restype = _I
     _D = ctypes.c_double
-    L.sink_attn_rope_table.argtypes = [_P, _I, _I, _D, _D, _I, _D, _D, _D, _P]
+    L.sink_attn_rope_table.argtypes = [_P, _I, _I, _D, _D, _I, _D, _D, _D, ctypes.c_int, _P]
     L.sink_attn_rope_table.restype = ctypes.c_int
     L.sink_attn_qkv_rope_append.argtypes = [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                             _I, _I, _P, _P, _P, _P]
@@ -326,12 +326,17 @@ def sink_attn_verify_tree(q, qo_indptr, draft_mask, k_pages, v_pages, page_indpt
         _stream(stream)))
 
 
+YARN_RAMP_TURNS = 0
+YARN_RAMP_PAIRS = 1
+
+
 def sink_attn_rope_table(table, max_pos, head_dim, rope_theta, factor, original_max_pos,
-                         beta_fast, beta_slow, attn_factor=0.0, stream=None) -> None:
+                         beta_fast, beta_slow, attn_factor=0.0, yarn_ramp=YARN_RAMP_TURNS,
+                         stream=None) -> None:
     _check(lib().sink_attn_rope_table(
         _ptr(table), int(max_pos), int(head_dim), float(rope_theta), float(factor),
         int(original_max_pos), float(beta_fast), float(beta_slow), float(attn_factor),
-        _stream(stream)))
+        int(yarn_ramp), _stream(stream)))
 
 
 def sink_attn_qkv_rope_append(qkv, bias, rope_table, max_pos, qo_indptr, kv_len, page_indptr,

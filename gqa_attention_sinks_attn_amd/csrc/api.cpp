@@ -899,7 +899,8 @@ sink_attn_status sink_attn_verify_tree(const void* q, const int32_t* qo_indptr,
 sink_attn_status sink_attn_rope_table(float* table, int32_t max_pos, int32_t head_dim,
                                       double rope_theta, double factor,
                                       int32_t original_max_pos, double beta_fast,
-                                      double beta_slow, double attn_factor, void* stream) {
+                                      double beta_slow, double attn_factor,
+                                      sink_attn_yarn_ramp yarn_ramp, void* stream) {
   if (!table) return fail(SINK_ATTN_ERR_NULL_ARG, "rope_table: table is required");
   if (max_pos < 1) return fail(SINK_ATTN_ERR_BAD_SHAPE, "rope_table: max_pos=%d", max_pos);
   if (head_dim != kHeadDim)
@@ -913,6 +914,8 @@ sink_attn_status sink_attn_rope_table(float* table, int32_t max_pos, int32_t hea
     return fail(SINK_ATTN_ERR_BAD_SHAPE,
                 "rope_table: YaRN needs original_max_pos >= 1 and 0 < beta_slow < beta_fast "
                 "(got %d, %g, %g)", original_max_pos, beta_slow, beta_fast);
+  if (yarn_ramp != SINK_ATTN_YARN_RAMP_TURNS && yarn_ramp != SINK_ATTN_YARN_RAMP_PAIRS)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "rope_table: unknown yarn_ramp %d", (int)yarn_ramp);
   if (!aligned(table, 16)) return fail(SINK_ATTN_ERR_MISALIGNED, "rope_table: table must be 16-byte aligned");
   sa::RopeTableArgs a;
   a.table = table;
@@ -923,6 +926,18 @@ sink_attn_status sink_attn_rope_table(float* table, int32_t max_pos, int32_t hea
   a.beta_fast = beta_fast;
   a.beta_slow = beta_slow;
   a.temperature = attn_factor > 0.0 ? attn_factor : (factor > 1.0 ? 0.1 * std::log(factor) + 1.0 : 1.0);
+  a.pair_ramp = yarn_ramp == SINK_ATTN_YARN_RAMP_PAIRS ? 1 : 0;
+  if (a.pair_ramp && factor > 1.0) {
+    // the rounded pairs that turn beta_fast and beta_slow times in L
+    auto pair_of = [&](double turns) {
+      return kHeadDim * std::log(original_max_pos / (6.283185307179586 * turns)) /
+             (2.0 * std::log(rope_theta));
+    };
+    a.ramp_low = std::max(std::floor(pair_of(beta_fast)), 0.0);
+    a.ramp_high = std::min(std::ceil(pair_of(beta_slow)), kHeadDim / 2 - 1.0);
+  } else {
+    a.ramp_low = a.ramp_high = 0.0;
+  }
   return hip_status(sa::launch_rope_table(a, static_cast<hipStream_t>(stream)), "rope_table launch");
 }
 

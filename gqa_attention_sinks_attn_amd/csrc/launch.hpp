@@ -127,6 +127,8 @@ struct RopeTableArgs {
   int32_t max_pos;
   int32_t original_max_pos;
   double base, factor, beta_fast, beta_slow, temperature;
+  int32_t pair_ramp;            // 0: blend linear in the turn count; 1: in the pair index
+  double ramp_low, ramp_high;   // pair-index ramp: the rounded bounds
 };
 
 struct RopeAppendArgs {

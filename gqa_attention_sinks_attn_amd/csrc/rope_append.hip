@@ -8,8 +8,10 @@
 // 2023): per pair d the base frequency base^(-2d/D) is kept when the pair
 // turns more than beta_fast times within the original context length L,
 // divided by the scale factor s when it turns fewer than beta_slow times, and
-// blended linearly in the turn count between the two; q and k are both
-// multiplied by the temperature 0.1 ln s + 1.  "Accelerating Sonar Through
+// blended linearly between the two, in the turn count (the paper's formula)
+// or in the pair index between the rounded bounds (DeepSeek-V3's code, which
+// the page names); q and k are both multiplied by the temperature
+// 0.1 ln s + 1.  "Accelerating Sonar Through
 // Speculation" (Perplexity), "Inference with Speculative Decoding": the
 // scheduler reserves room for the next tokens in the paged cache before the
 // step runs; token t of a request with qlen new tokens and kv_len keys
@@ -49,11 +51,17 @@ __global__ __launch_bounds__(256) void rope_table_kernel(RopeTableArgs a) {
   const double theta = pow(a.base, -2.0 * d / kD);
   double f = theta;
   if (a.factor > 1.0) {
-    const double turns = a.original_max_pos * theta / kTwoPi;   // L / wavelength
     double keep;   // 1: keep theta, 0: theta / factor
-    if (turns < a.beta_slow) keep = 0.0;
-    else if (turns > a.beta_fast) keep = 1.0;
-    else keep = (turns - a.beta_slow) / (a.beta_fast - a.beta_slow);
+    if (a.pair_ramp) {
+      // linear in the pair index between the rounded correction pairs
+      if (a.ramp_high <= a.ramp_low) keep = d <= a.ramp_low ? 1.0 : 0.0;
+      else keep = fmin(fmax(1.0 - (d - a.ramp_low) / (a.ramp_high - a.ramp_low), 0.0), 1.0);
+    } else {
+      const double turns = a.original_max_pos * theta / kTwoPi;   // L / wavelength
+      if (turns < a.beta_slow) keep = 0.0;
+      else if (turns > a.beta_fast) keep = 1.0;
+      else keep = (turns - a.beta_slow) / (a.beta_fast - a.beta_slow);
+    }
     f = (1.0 - keep) * theta / a.factor + keep * theta;
   }
   const double angle = (double)p * f;

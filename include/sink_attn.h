@@ -462,16 +462,33 @@ sink_attn_status sink_attn_verify_tree(
  *                    YaRN's L, beta and alpha (used when s > 1): pair d keeps
  *                    f_d when it turns more than beta_fast times in L tokens,
  *                    gets f_d / s when it turns fewer than beta_slow times,
- *                    and a linear blend in the turn count between.
+ *                    and a blend of the two between.
  *   attn_factor      T; 0 selects 0.1 ln s + 1 (1 when s <= 1).
+ *   yarn_ramp        the blend between the two bounds:
+ *                    SINK_ATTN_YARN_RAMP_TURNS (0): linear in the turn count
+ *                    r_d = L f_d / (2 pi), as the YaRN paper writes it;
+ *                    SINK_ATTN_YARN_RAMP_PAIRS (1): linear in the pair index
+ *                    between low = floor(d(beta_fast)) and high =
+ *                    ceil(d(beta_slow)), d(r) = 64 ln(L / (2 pi r)) /
+ *                    (2 ln theta) the pair that turns r times (clamped to
+ *                    0 .. 31; a step at low when high <= low), as DeepSeek-V3,
+ *                    which the page names, and the YaRN authors' code do.
+ *                    The two agree on which pairs keep, blend or divide by
+ *                    s.  Other values: SINK_ATTN_ERR_UNSUPPORTED.
  * Angles and sin/cos are evaluated in fp64.  SINK_ATTN_ERR_BAD_SHAPE for
  * max_pos < 1, theta <= 1, factor <= 0, attn_factor < 0, or (s > 1)
  * original_max_pos < 1 or not 0 < beta_slow < beta_fast.
  */
+typedef enum {
+  SINK_ATTN_YARN_RAMP_TURNS = 0,
+  SINK_ATTN_YARN_RAMP_PAIRS = 1
+} sink_attn_yarn_ramp;
+
 sink_attn_status sink_attn_rope_table(float* table, int32_t max_pos, int32_t head_dim,
                                       double rope_theta, double factor,
                                       int32_t original_max_pos, double beta_fast,
-                                      double beta_slow, double attn_factor, void* stream);
+                                      double beta_slow, double attn_factor,
+                                      sink_attn_yarn_ramp yarn_ramp, void* stream);
 
 /*
  * sink_attn_qkv_rope_append: for every new token, add the bias to its fused

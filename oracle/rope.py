@@ -23,6 +23,15 @@ What the pages fix, and the readings taken where they stop:
     i.e. to every cos and sin.  s <= 1 is plain rotary encoding (no change,
     temperature 1).  base, s, L, alpha (beta_slow) and beta (beta_fast) are
     parameters;
+  - "like DeepSeek-V3": DeepSeek-V3 (and the YaRN authors' released code)
+    blend linearly in the pair index instead of the rotation count: the
+    pair d at which the wavelength fits r turns in L is d(r) = D ln(L /
+    (2 pi r)) / (2 ln base); with low = floor(d(beta)) and high =
+    ceil(d(alpha)) (clamped to the pairs that exist), gamma(d) = 1 - (d -
+    low) / (high - low), clamped to [0, 1] (a step at low when high <= low).
+    Both ramps are offered ("turns", the published formula, and "pairs");
+    they agree on which pairs keep, ramp or divide by s, and differ in the
+    blend of the ramped pairs;
   - pairing: the pages do not say which dimensions form a rotated pair.
     "half" rotates dimension i with i + D/2 (the rotate-half layout),
     "interleaved" rotates 2i with 2i + 1 (the complex-pair layout); both
@@ -55,24 +64,43 @@ def _bf16_to_f64(bits):
         .view(np.float32).astype(np.float64)
 
 
+def correction_pair(rotations: float, head_dim: int, base: float, original_max_pos: int) -> float:
+    """The fractional pair index whose wavelength 2 pi base^(2d/D) fits
+    `rotations` turns in the original context."""
+    return head_dim * math.log(original_max_pos / (2.0 * math.pi * rotations)) / (2.0 * math.log(base))
+
+
 def yarn_frequencies(head_dim: int, base: float, factor: float, original_max_pos: int,
-                     beta_fast: float, beta_slow: float) -> np.ndarray:
-    """Rotary frequency of each of the head_dim / 2 pairs (YaRN, NTK-by-parts)."""
+                     beta_fast: float, beta_slow: float, ramp: str = "turns") -> np.ndarray:
+    """Rotary frequency of each of the head_dim / 2 pairs (YaRN, NTK-by-parts).
+    ramp: "turns" blends linearly in the rotation count, "pairs" linearly in
+    the pair index between the rounded correction pairs."""
+    if ramp not in ("turns", "pairs"):
+        raise ValueError(ramp)
     half = head_dim // 2
     out = np.zeros(half)
+    if ramp == "pairs" and factor > 1.0:
+        low = max(math.floor(correction_pair(beta_fast, head_dim, base, original_max_pos)), 0)
+        high = min(math.ceil(correction_pair(beta_slow, head_dim, base, original_max_pos)), half - 1)
     for d in range(half):
         theta = base ** (-2.0 * d / head_dim)
         if factor <= 1.0:
             out[d] = theta
             continue
-        wavelength = 2.0 * math.pi / theta
-        r = original_max_pos / wavelength          # rotations within the original context
-        if r < beta_slow:
-            gamma = 0.0                            # long wavelengths: interpolate fully
-        elif r > beta_fast:
-            gamma = 1.0                            # short wavelengths: keep
+        if ramp == "pairs":
+            if high <= low:
+                gamma = 1.0 if d <= low else 0.0
+            else:
+                gamma = min(max(1.0 - (d - low) / (high - low), 0.0), 1.0)
         else:
-            gamma = (r - beta_slow) / (beta_fast - beta_slow)
+            wavelength = 2.0 * math.pi / theta
+            r = original_max_pos / wavelength      # rotations within the original context
+            if r < beta_slow:
+                gamma = 0.0                        # long wavelengths: interpolate fully
+            elif r > beta_fast:
+                gamma = 1.0                        # short wavelengths: keep
+            else:
+                gamma = (r - beta_slow) / (beta_fast - beta_slow)
         out[d] = (1.0 - gamma) * theta / factor + gamma * theta
     return out
 
@@ -83,10 +111,11 @@ def yarn_temperature(factor: float) -> float:
 
 
 def rope_table(max_pos: int, head_dim: int, base: float, factor: float, original_max_pos: int,
-               beta_fast: float, beta_slow: float, attn_factor: float = 0.0) -> np.ndarray:
+               beta_fast: float, beta_slow: float, attn_factor: float = 0.0,
+               ramp: str = "turns") -> np.ndarray:
     """[max_pos, head_dim]: temperature * cos(p f_d) in column d, temperature *
     sin(p f_d) in column head_dim/2 + d.  attn_factor <= 0: YaRN's own."""
-    f = yarn_frequencies(head_dim, base, factor, original_max_pos, beta_fast, beta_slow)
+    f = yarn_frequencies(head_dim, base, factor, original_max_pos, beta_fast, beta_slow, ramp)
     m = attn_factor if attn_factor > 0 else yarn_temperature(factor)
     half = head_dim // 2
     tab = np.zeros((max_pos, head_dim))

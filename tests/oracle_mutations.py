@@ -95,6 +95,12 @@ MUTATIONS = [
     ("rotated pairings swapped", ROPE, "    if interleaved:\n", "    if not interleaved:\n"),
     ("frequency exponent halved", ROPE,
      "theta = base ** (-2.0 * d / head_dim)", "theta = base ** (-1.0 * d / head_dim)"),
+    ("pair ramp bounds rounded the wrong way", ROPE,
+     "low = max(math.floor(correction_pair(beta_fast, head_dim, base, original_max_pos)), 0)",
+     "low = max(math.ceil(correction_pair(beta_fast, head_dim, base, original_max_pos)), 0)"),
+    ("pair ramp blended the wrong way", ROPE,
+     "gamma = min(max(1.0 - (d - low) / (high - low), 0.0), 1.0)",
+     "gamma = min(max((d - low) / (high - low), 0.0), 1.0)"),
     ("append to the page of the next position", ROPE,
      "page = int(page_indices[int(page_indptr[b]) + p // page_size])",
      "page = int(page_indices[int(page_indptr[b]) + (p + 1) // page_size])"),

@@ -430,18 +430,19 @@ def test_verify_tree_empty_call_is_ok():
 
 def call_rope_table(**over):
     a = dict(table=A, max_pos=4096, head_dim=64, theta=150000.0, factor=32.0, orig=4096,
-             beta_fast=32.0, beta_slow=1.0, attn_factor=0.0, stream=0)
+             beta_fast=32.0, beta_slow=1.0, attn_factor=0.0, ramp=0, stream=0)
     a.update(over)
     return sa.lib().sink_attn_rope_table(a["table"], a["max_pos"], a["head_dim"], a["theta"],
                                          a["factor"], a["orig"], a["beta_fast"], a["beta_slow"],
-                                         a["attn_factor"], a["stream"])
+                                         a["attn_factor"], a["ramp"], a["stream"])
 
 
 @pytest.mark.parametrize("over,code", [
     (dict(table=None), NULL), (dict(max_pos=0), SHAPE), (dict(head_dim=128), UNSUP),
     (dict(theta=1.0), SHAPE), (dict(factor=0.0), SHAPE), (dict(attn_factor=-1.0), SHAPE),
     (dict(orig=0), SHAPE), (dict(beta_fast=1.0), SHAPE), (dict(beta_slow=0.0), SHAPE),
-    (dict(theta=float("inf")), SHAPE), (dict(table=A + 4), MISAL),
+    (dict(theta=float("inf")), SHAPE), (dict(table=A + 4), MISAL), (dict(ramp=2), UNSUP),
+    (dict(ramp=-1), UNSUP),
 ])
 def test_rope_table_rejects(over, code):
     assert call_rope_table(**over) == code

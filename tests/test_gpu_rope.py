@@ -41,37 +41,44 @@ def _i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
 
 
-def _ref_table(max_pos, cfg, attn_factor=0.0):
+def _ref_table(max_pos, cfg, attn_factor=0.0, ramp="turns"):
     return rope.rope_table(max_pos, 64, cfg["rope_theta"], cfg["factor"], cfg["original_max_pos"],
-                           cfg["beta_fast"], cfg["beta_slow"], attn_factor)
+                           cfg["beta_fast"], cfg["beta_slow"], attn_factor, ramp)
 
 
-def _gpu_table(max_pos, cfg, attn_factor=0.0):
-    from gqa_attention_sinks_attn_amd import sink_attn_rope_table
+def _gpu_table(max_pos, cfg, attn_factor=0.0, ramp="turns"):
+    from gqa_attention_sinks_attn_amd import (YARN_RAMP_PAIRS, YARN_RAMP_TURNS,
+                                              sink_attn_rope_table)
     t = torch.full((max_pos, 64), float("nan"), dtype=torch.float32, device="cuda")
     sink_attn_rope_table(t, max_pos, 64, cfg["rope_theta"], cfg["factor"],
-                         cfg["original_max_pos"], cfg["beta_fast"], cfg["beta_slow"], attn_factor)
+                         cfg["original_max_pos"], cfg["beta_fast"], cfg["beta_slow"], attn_factor,
+                         YARN_RAMP_PAIRS if ramp == "pairs" else YARN_RAMP_TURNS)
     torch.cuda.synchronize()
     return t
 
 
-@pytest.mark.parametrize("cfg,attn_factor", [
-    (YARN, 0.0),
-    (YARN, 1.0),
-    (dict(rope_theta=10000.0, factor=1.0, original_max_pos=0, beta_fast=0.0, beta_slow=0.0), 0.0),
-    (dict(rope_theta=10000.0, factor=8.0, original_max_pos=2048, beta_fast=16.0, beta_slow=2.0), 0.0),
+@pytest.mark.parametrize("cfg,attn_factor,ramp", [
+    (YARN, 0.0, "turns"),
+    (YARN, 1.0, "turns"),
+    (YARN, 0.0, "pairs"),
+    (dict(rope_theta=10000.0, factor=1.0, original_max_pos=0, beta_fast=0.0, beta_slow=0.0), 0.0,
+     "turns"),
+    (dict(rope_theta=10000.0, factor=8.0, original_max_pos=2048, beta_fast=16.0, beta_slow=2.0), 0.0,
+     "turns"),
+    (dict(rope_theta=10000.0, factor=8.0, original_max_pos=2048, beta_fast=16.0, beta_slow=2.0), 0.0,
+     "pairs"),
 ])
-def test_rope_table_matches_oracle(cfg, attn_factor):
+def test_rope_table_matches_oracle(cfg, attn_factor, ramp):
     max_pos = 131072
-    t = _gpu_table(max_pos, cfg, attn_factor).cpu().numpy().astype(np.float64)
+    t = _gpu_table(max_pos, cfg, attn_factor, ramp).cpu().numpy().astype(np.float64)
     temp = attn_factor if attn_factor > 0 else rope.yarn_temperature(cfg["factor"])
-    first = _ref_table(2048, cfg, attn_factor)
+    first = _ref_table(2048, cfg, attn_factor, ramp)
     err = np.abs(t[:2048] - first).max()
-    print(f"[rope table {cfg['factor']}] first 2048 positions max err {err:.3e}", flush=True)
+    print(f"[rope table {cfg['factor']} {ramp}] first 2048 positions max err {err:.3e}", flush=True)
     assert err <= 2.0 ** -23 * temp
     # large positions, where the angle reaches 1e5 rad
     f = rope.yarn_frequencies(64, cfg["rope_theta"], cfg["factor"], cfg["original_max_pos"],
-                              cfg["beta_fast"], cfg["beta_slow"])
+                              cfg["beta_fast"], cfg["beta_slow"], ramp)
     rng = np.random.default_rng(5)
     for p in list(rng.integers(2048, max_pos, size=200)) + [max_pos - 1]:
         ref = np.concatenate([temp * np.cos(p * f), temp * np.sin(p * f)])

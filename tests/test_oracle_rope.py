@@ -174,3 +174,47 @@ def test_no_bias_and_sampled_rows():
     v = bf16_bits_to_f32(ab.qkv).astype(np.float64)[:, 5]
     page = ab.page_indices[ab.page_indptr[1]]
     np.testing.assert_array_equal(vc[page, 0, :6], v[4:10])
+
+
+def test_golden_pair_ramp():
+    """The pair-index ramp: rounded correction pairs, the same keep / ramp /
+    interpolate classes as the rotation-count ramp, and a hand-derived blend
+    of one ramped pair under each ramp."""
+    g = json.load(open(GOLDEN))["pair_ramp"]
+    for c in g["cases"]:
+        D, base, s, L = c["head_dim"], c["base"], c["factor"], c["original_max_pos"]
+        args = (D, base, s, L, c["beta_fast"], c["beta_slow"])
+        assert math.floor(rope.correction_pair(c["beta_fast"], D, base, L)) == c["low"]
+        assert math.ceil(rope.correction_pair(c["beta_slow"], D, base, L)) == c["high"]
+        fp = rope.yarn_frequencies(*args, ramp="pairs")
+        ft = rope.yarn_frequencies(*args, ramp="turns")
+        theta = base ** (-2.0 * np.arange(D // 2) / D)
+        k0, k1 = c["kept"]
+        i0, i1 = c["interpolated"]
+        r0, r1 = c["ramped"]
+        for f in (fp, ft):
+            np.testing.assert_allclose(f[k0:k1 + 1], theta[k0:k1 + 1], rtol=1e-15, atol=0)
+            np.testing.assert_allclose(f[i0:i1 + 1], theta[i0:i1 + 1] / s, rtol=1e-15, atol=0)
+            mid = slice(r0, r1 + 1)
+            assert np.all(f[mid] > theta[mid] / s) and np.all(f[mid] < theta[mid])
+        d = c["pair"]
+        assert abs(theta[d] - c["theta"]) <= 1e-15
+        assert abs(fp[d] - c["pairs_frequency"]) <= 1e-15
+        assert abs(ft[d] - c["turns_frequency"]) <= 1e-15
+        # linear in the pair index: equal steps of the kept fraction
+        keep = (fp - theta / s) / (theta - theta / s)
+        steps = np.diff(keep[c["low"]:c["high"] + 1])
+        np.testing.assert_allclose(steps, -1.0 / (c["high"] - c["low"]), rtol=1e-12)
+
+
+def test_pair_ramp_degenerate_range_is_a_step():
+    """When the rounded correction pairs leave no room for a ramp (high <=
+    low) the blend is a step: pairs up to low keep, the rest divide by s.
+    With beta_fast = 1e6 turns, d(beta) is negative, so low clamps to pair 0
+    and high (also negative) falls below it."""
+    D, base, s, L = 64, 10000.0, 4.0, 4096
+    assert rope.correction_pair(1e6, D, base, L) < -25
+    f = rope.yarn_frequencies(D, base, s, L, 1e6, 1e6 - 1e-3, ramp="pairs")
+    theta = base ** (-2.0 * np.arange(D // 2) / D)
+    assert f[0] == theta[0]
+    np.testing.assert_allclose(f[1:], theta[1:] / s, rtol=1e-15)
