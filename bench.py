@@ -494,7 +494,12 @@ def graph_step_line(torch, sa, W, res, steps, warm):
         sa.sink_attn_decode(q, kp, vp, pi, px, kl, sinks, B, Hq, Hkv, 64, 16, max_L, 0, 0.125, out,
                             sa.F32, lse, ws, ws_bytes)
 
+    def attend(i=0):
+        sa.sink_attn_decode(q, kp, vp, pi, px, kl, sinks, B, Hq, Hkv, 64, 16, max_L, 0, 0.125, out,
+                            sa.F32, lse, ws, ws_bytes)
+
     eager = _time_calls(torch, call, steps, warm)
+    attend_only = _time_calls(torch, attend, steps, warm)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         call()
@@ -508,7 +513,8 @@ def graph_step_line(torch, sa, W, res, steps, warm):
     res["decode_step_graph"] = dict(
         workload=f"decode step: B={B}, L~U[1,4096], 64q/8kv; append + attend",
         call="sink_attn_qkv_rope_append + sink_attn_decode (balanced), 3 kernels",
-        ms_eager=round(eager, 5), ms_graph_replay=round(replay, 5),
+        ms_eager=round(eager, 5), ms_attend_only=round(attend_only, 5),
+        ms_graph_replay=round(replay, 5),
         kv_gbs_graph=round(kv / (replay * 1e-3) / 1e9, 1))
     del graph
 
