@@ -62,11 +62,11 @@ CSRC = os.path.join(ROOT, "gqa_attention_sinks_attn_amd", "csrc")
 # kernel and by the hash of the sources that build it.  A source change
 # makes the figure stale: it is then reported as null until retaken.
 TRAFFIC = {
-    "c2": (260_943_357, "decode_balanced.hip", "ea1a589be33c338f"),
-    "c3": (1_076_443_896, "decode_balanced.hip", "ea1a589be33c338f"),
-    "c4": (1_876_166_305, "prefill.hip", "c1ce4f8779e81c77"),
-    "c5_prefill": (6_378_097_745, "prefill.hip", "c1ce4f8779e81c77"),
-    "c5_decode": (4_355_372_852, "decode_balanced.hip", "ea1a589be33c338f"),
+    "c2": (260_943_357, "decode_balanced.hip", "9a447f3f65222092"),
+    "c3": (1_076_443_896, "decode_balanced.hip", "9a447f3f65222092"),
+    "c4": (1_876_166_305, "prefill.hip", "4505943ee4bbf007"),
+    "c5_prefill": (6_378_097_745, "prefill.hip", "4505943ee4bbf007"),
+    "c5_decode": (4_355_372_852, "decode_balanced.hip", "9a447f3f65222092"),
 }
 
 
@@ -498,17 +498,31 @@ def graph_step_line(torch, sa, W, res, steps, warm):
         sa.sink_attn_decode(q, kp, vp, pi, px, kl, sinks, B, Hq, Hkv, 64, 16, max_L, 0, 0.125, out,
                             sa.F32, lse, ws, ws_bytes)
 
+    fws_bytes = sa.sink_attn_decode_step_workspace_size(B, Hq, Hkv, 64, max_L)
+    fws = torch.empty(max(fws_bytes, 256), dtype=torch.uint8, device="cuda")
+
+    def fused(i=0):
+        sa.sink_attn_decode_step(qkv, bias, table, 4096, 0, kp, vp, pi, px, kl, sinks, B, Hq, Hkv,
+                                 64, 16, max_L, 0.125, out, sa.F32, lse, fws, fws_bytes)
+
+    def replayed(fn):
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            fn()
+        stream.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            fn()
+        torch.cuda.synchronize()
+        ms = _time_calls(torch, lambda i: graph.replay(), steps, warm)
+        del graph
+        return ms
+
     eager = _time_calls(torch, call, steps, warm)
     attend_only = _time_calls(torch, attend, steps, warm)
-    stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        call()
-    stream.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        call()
-    torch.cuda.synchronize()
-    replay = _time_calls(torch, lambda i: graph.replay(), steps, warm)
+    fused_eager = _time_calls(torch, fused, steps, warm)
+    replay = replayed(call)
+    fused_replay = replayed(fused)
     kv = int(L.sum()) * 2 * Hkv * 64 * 2
     res["decode_step_graph"] = dict(
         workload=f"decode step: B={B}, L~U[1,4096], 64q/8kv; append + attend",
@@ -516,7 +530,11 @@ def graph_step_line(torch, sa, W, res, steps, warm):
         ms_eager=round(eager, 5), ms_attend_only=round(attend_only, 5),
         ms_graph_replay=round(replay, 5),
         kv_gbs_graph=round(kv / (replay * 1e-3) / 1e9, 1))
-    del graph
+    res["decode_step_fused"] = dict(
+        workload=f"decode step: B={B}, L~U[1,4096], 64q/8kv; append + attend",
+        call="sink_attn_decode_step (the append inside the balanced first pass), 2 kernels",
+        ms_eager=round(fused_eager, 5), ms_graph_replay=round(fused_replay, 5),
+        kv_gbs=round(kv / (fused_eager * 1e-3) / 1e9, 1))
 
 
 def append_lines(args, torch, sa, W, res, steps, warm):

@@ -25,7 +25,8 @@ __all__ = [
     "sink_attn_decode_balanced_finish", "sink_attn_decode_balanced_workspace_size",
     "sink_attn_decode_num_ranges", "sink_attn_verify", "sink_attn_verify_workspace_size",
     "sink_attn_verify_tree", "sink_attn_verify_num_splits", "sink_attn_rope_table",
-    "sink_attn_qkv_rope_append", "sink_attn_decode_noalloc",
+    "sink_attn_qkv_rope_append", "sink_attn_decode_noalloc", "sink_attn_decode_step",
+    "sink_attn_decode_step_workspace_size",
     "sink_attn_status_string", "sink_attn_last_error", "sink_attn_version",
     "SYMBOLS",
 ]
@@ -40,7 +41,8 @@ SYMBOLS = (
     "sink_attn_decode_balanced_finish", "sink_attn_decode_balanced_workspace_size",
     "sink_attn_decode_num_ranges", "sink_attn_verify", "sink_attn_verify_workspace_size",
     "sink_attn_verify_tree", "sink_attn_verify_num_splits", "sink_attn_rope_table",
-    "sink_attn_qkv_rope_append", "sink_attn_decode_noalloc",
+    "sink_attn_qkv_rope_append", "sink_attn_decode_noalloc", "sink_attn_decode_step",
+    "sink_attn_decode_step_workspace_size",
     "sink_attn_status_string", "sink_attn_last_error", "sink_attn_version",
 )
 
@@ -116,6 +118,12 @@ def lib():
     L.sink_attn_qkv_rope_append.argtypes = [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                             _I, _I, _P, _P, _P, _P]
     L.sink_attn_qkv_rope_append.restype = ctypes.c_int
+    L.sink_attn_decode_step.argtypes = [_P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I,
+                                        _I, _I, _I, ctypes.c_float, _P, ctypes.c_int, _P, _P,
+                                        ctypes.c_size_t, _P]
+    L.sink_attn_decode_step.restype = ctypes.c_int
+    L.sink_attn_decode_step_workspace_size.argtypes = [_I, _I, _I, _I, _I]
+    L.sink_attn_decode_step_workspace_size.restype = ctypes.c_size_t
     L.sink_attn_status_string.argtypes = [ctypes.c_int]
     L.sink_attn_status_string.restype = ctypes.c_char_p
     L.sink_attn_last_error.argtypes = []
@@ -337,6 +345,24 @@ def sink_attn_rope_table(table, max_pos, head_dim, rope_theta, factor, original_
         _ptr(table), int(max_pos), int(head_dim), float(rope_theta), float(factor),
         int(original_max_pos), float(beta_fast), float(beta_slow), float(attn_factor),
         int(yarn_ramp), _stream(stream)))
+
+
+def sink_attn_decode_step_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim,
+                                         max_kv_len) -> int:
+    return int(lib().sink_attn_decode_step_workspace_size(
+        int(batch), int(num_qo_heads), int(num_kv_heads), int(head_dim), int(max_kv_len)))
+
+
+def sink_attn_decode_step(qkv, bias, rope_table, max_pos, interleaved, k_pages, v_pages,
+                          page_indptr, page_indices, kv_len, sinks, batch, num_qo_heads,
+                          num_kv_heads, head_dim, page_size, max_kv_len, sm_scale, out, out_dtype,
+                          lse, workspace, workspace_bytes, stream=None) -> None:
+    _check(lib().sink_attn_decode_step(
+        _ptr(qkv), _ptr(bias), _ptr(rope_table), int(max_pos), int(interleaved), _ptr(k_pages),
+        _ptr(v_pages), _ptr(page_indptr), _ptr(page_indices), _ptr(kv_len), _ptr(sinks),
+        int(batch), int(num_qo_heads), int(num_kv_heads), int(head_dim), int(page_size),
+        int(max_kv_len), float(sm_scale), _ptr(out), _dtype_code(out_dtype), _ptr(lse),
+        _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def sink_attn_qkv_rope_append(qkv, bias, rope_table, max_pos, qo_indptr, kv_len, page_indptr,

@@ -139,6 +139,8 @@ RangePlan plan_ranges(int32_t batch, int32_t hkv, int32_t max_kv_len, int32_t re
 
 size_t balanced_slots(int32_t batch, int32_t n_ranges) { return (size_t)n_ranges + batch - 1; }
 
+size_t align_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+
 // sink_attn_decode's automatic plan: requests longer than 16 pages go to the
 // load-balanced plan; shorter ones fit one chunk, written by one kernel.
 bool auto_uses_balanced(int32_t max_kv_len, int32_t num_splits) {
@@ -556,6 +558,14 @@ sink_attn_status balanced_setup(const void* q, const void* k_pages, const void* 
   a->lse_part = reinterpret_cast<float*>(
       static_cast<char*>(workspace) +
       balanced_slots(batch, plan.n_ranges) * num_qo_heads * head_dim * sizeof(float));
+  a->qkv = nullptr;   // a plain decode; the decode step sets these
+  a->bias = nullptr;
+  a->table = nullptr;
+  a->max_pos = 0;
+  a->interleaved = 0;
+  a->k_new = nullptr;
+  a->v_new = nullptr;
+  a->q_new = nullptr;
   return ok();
 }
 
@@ -610,6 +620,61 @@ sink_attn_status sink_attn_decode_balanced(
                   "decode_balanced launch");
   if (st != SINK_ATTN_OK) return st;
   return hip_status(sa::launch_decode_finish(a, s), "decode_balanced finish launch");
+}
+
+size_t sink_attn_decode_step_workspace_size(int32_t batch, int32_t num_qo_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t max_kv_len) {
+  const size_t partials = sink_attn_decode_balanced_workspace_size(batch, num_qo_heads,
+                                                                   num_kv_heads, head_dim,
+                                                                   max_kv_len, 0);
+  if (batch <= 0 || num_qo_heads <= 0 || head_dim != kHeadDim) return partials;
+  return align_up(partials, 256) + (size_t)batch * num_qo_heads * head_dim * sizeof(uint16_t);
+}
+
+sink_attn_status sink_attn_decode_step(
+    const void* qkv, const void* bias, const float* rope_table, int32_t max_pos,
+    int32_t interleaved, void* k_pages, void* v_pages, const int32_t* page_indptr,
+    const int32_t* page_indices, const int32_t* kv_len, const float* sinks, int32_t batch,
+    int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+    int32_t max_kv_len, float sm_scale, void* out, sink_attn_dtype out_dtype, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!qkv || !rope_table)
+    return fail(SINK_ATTN_ERR_NULL_ARG, "decode_step: qkv and rope_table are required");
+  if (max_pos < 1) return fail(SINK_ATTN_ERR_BAD_SHAPE, "decode_step: max_pos=%d", max_pos);
+  if (interleaved != 0 && interleaved != 1)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "decode_step: interleaved must be 0 or 1");
+  if ((bias && !aligned(bias, 16)) || !aligned(rope_table, 16))
+    return fail(SINK_ATTN_ERR_MISALIGNED, "decode_step: bias and rope_table must be 16-byte aligned");
+  // qkv stands in for q in the decode's checks (non-NULL, 16-byte aligned)
+  sa::BalancedDecodeArgs a;
+  sink_attn_status st = balanced_setup(qkv, k_pages, v_pages, page_indptr, page_indices, kv_len,
+                                       sinks, batch, num_qo_heads, num_kv_heads, head_dim,
+                                       page_size, max_kv_len, 0, sm_scale, out, out_dtype, lse,
+                                       workspace, workspace_bytes, 3, &a);
+  if (st != SINK_ATTN_OK) return st;
+  const size_t need = sink_attn_decode_step_workspace_size(batch, num_qo_heads, num_kv_heads,
+                                                           head_dim, max_kv_len);
+  if (workspace_bytes < need)
+    return fail(SINK_ATTN_ERR_WORKSPACE, "decode_step: workspace of %zu bytes < %zu needed",
+                workspace_bytes, need);
+  a.q_new = reinterpret_cast<uint16_t*>(
+      static_cast<char*>(workspace) +
+      align_up(sink_attn_decode_balanced_workspace_size(batch, num_qo_heads, num_kv_heads,
+                                                        head_dim, max_kv_len, 0), 256));
+  a.q = a.q_new;
+  a.qkv = static_cast<const uint16_t*>(qkv);
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.table = rope_table;
+  a.max_pos = max_pos;
+  a.interleaved = interleaved;
+  a.k_new = static_cast<uint16_t*>(k_pages);
+  a.v_new = static_cast<uint16_t*>(v_pages);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(sa::launch_decode_balanced(a, num_qo_heads / num_kv_heads, s),
+                  "decode_step launch");
+  if (st != SINK_ATTN_OK) return st;
+  return hip_status(sa::launch_decode_finish(a, s), "decode_step finish launch");
 }
 
 namespace {

@@ -52,6 +52,23 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Rotation of one rotary pair (u, v) by the angle whose cosine and sine
+// (both times the attention temperature) are c and s: (u c - v s, v c + u s).
+// Each output is one rounded product and one fused multiply-add, written out
+// with contraction off, so that every kernel that rotates a token rounds it
+// identically (the decode step's fused append must reproduce the append
+// kernel bit for bit).
+__device__ __forceinline__ void rotate_pair(float& u, float& v, float c, float s) {
+#pragma clang fp contract(off)
+  const float uu = u, vv = v;
+  const float vs = vv * s, us = uu * s;
+  u = __builtin_fmaf(uu, c, -vs);
+  v = __builtin_fmaf(vv, c, us);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return bf16_bits_to_float(w & 0xffffu); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return bf16_bits_to_float(w >> 16); }
+
 // D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.
 // A: lane l holds row l%16, eight k values; B: lane l holds column l%16,
 // the same eight k values; D: lane l holds column l%16, rows 4*(l/16)+i.

@@ -34,6 +34,19 @@
 // Stage 2 (decode_finish_kernel), one wave per (request, query head): merges
 // the partials of requests that span several ranges by log-sum-exp, and
 // writes requests without pages (o = 0, lse = sink).
+//
+// The decode step (STEP): stage 1 also does the step that precedes the
+// attention for each request's one new token ("Accelerating Sonar Through
+// Speculation", "Inference with Speculative Decoding": the new token's slot
+// is reserved in the paged cache before the step; "GPT-OSS on Day 0",
+// "Attention: GQA with attention sinks": QKV bias and YaRN rotary encoding).
+// Before it streams its range, a wave writes the new keys and values whose
+// cache slot lies in its own pages (for its KV head): it is the only reader
+// of those slots, so its later loads see them.  Each wave rotates the query
+// of every request it visits when it opens the segment (in the operand
+// layout a lane holds both members of each rotated pair).  The arithmetic is
+// the append kernel's, so the result equals the append followed by the
+// decode bit for bit.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -55,6 +68,44 @@ struct StepRegs {
   u32x4 k00, k01, k10, k11;   // K: page 0/1, dims 8 grp + {0, 32}
   u32x4 v00, v01, v10, v11;   // V: page 0/1, 32 contiguous bytes each
 };
+
+// One 16-byte piece of a new token's head, as the append kernel handles
+// it: dims off0 .. off0 + 3 and off1 .. off1 + 3 of lane j (off = 4 j and
+// 32 + 4 j in the rotate-half pairing, 8 j and 8 j + 4 interleaved), i.e.
+// rotary pairs 4 j .. 4 j + 3 in both; the bias added in fp32, the key and
+// query heads rotated by the token's table row (cos at 4 j, sin 32 floats
+// further), rounded to bf16 once.
+__device__ __forceinline__ void new_piece(u32x2 x0, u32x2 x1, u32x2 b0, u32x2 b1, bool rotate,
+                                          f32x4 c, f32x4 s, int interleaved, uint16_t* dst,
+                                          int off0, int off1) {
+  float lo[4] = {lo_bf16(x0[0]) + lo_bf16(b0[0]), hi_bf16(x0[0]) + hi_bf16(b0[0]),
+                 lo_bf16(x0[1]) + lo_bf16(b0[1]), hi_bf16(x0[1]) + hi_bf16(b0[1])};
+  float hi[4] = {lo_bf16(x1[0]) + lo_bf16(b1[0]), hi_bf16(x1[0]) + hi_bf16(b1[0]),
+                 lo_bf16(x1[1]) + lo_bf16(b1[1]), hi_bf16(x1[1]) + hi_bf16(b1[1])};
+  if (rotate) {
+    float u[4], v[4];
+    if (interleaved) {
+      u[0] = lo[0]; v[0] = lo[1]; u[1] = lo[2]; v[1] = lo[3];
+      u[2] = hi[0]; v[2] = hi[1]; u[3] = hi[2]; v[3] = hi[3];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { u[i] = lo[i]; v[i] = hi[i]; }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rotate_pair(u[i], v[i], c[i], s[i]);
+    if (interleaved) {
+      lo[0] = u[0]; lo[1] = v[0]; lo[2] = u[1]; lo[3] = v[1];
+      hi[0] = u[2]; hi[1] = v[2]; hi[2] = u[3]; hi[3] = v[3];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { lo[i] = u[i]; hi[i] = v[i]; }
+    }
+  }
+  *reinterpret_cast<u32x2*>(dst + off0) = u32x2{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3])};
+  *reinterpret_cast<u32x2*>(dst + off1) = u32x2{pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
+}
+
+__device__ __forceinline__ u32x2 ld8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 // Largest request b < B with indptr[b] <= pg (indptr non-decreasing,
 // indptr[0] = 0 <= pg): a 64-way sampled search, then a 64-way search inside
@@ -86,7 +137,7 @@ __device__ __forceinline__ int range_width(int nnz, int n_ranges, int min_pages)
   return max(min_pages, (nnz + n_ranges - 1) / n_ranges);
 }
 
-template <int G>
+template <int G, bool STEP>
 __global__ __launch_bounds__(256) void decode_balanced_kernel(BalancedDecodeArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[kWaves * kWaveLds];
 
@@ -108,12 +159,16 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(BalancedDecodeArgs
   if (p0 >= p1) return;
   const int n_steps = (p1 - p0 + 1) >> 1;
 
+  // (Every lambda of this kernel is forced inline: with the decode step's
+  // extra call sites the inliner would otherwise outline some of them, and
+  // an outlined helper works through the stack and generic pointers.)
+
   // Start-up.  Loads that need only the range go out first: the first 32
   // steps' page ids (lane l: page p0 + l, i.e. step l / 2, page l % 2), the
   // first level of the request lookup, and the head's sink.  The first
   // step's K/V loads follow as soon as the ids arrive, before the lookup
   // resolves, so the stream starts one round trip after the ids.
-  auto load_ids = [&](int first_step) {
+  auto load_ids = [&](int first_step) __attribute__((always_inline)) {
     return p.page_indices[min(p0 + 2 * first_step + lane, p1 - 1)];
   };
   int ids = load_ids(0);
@@ -126,7 +181,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(BalancedDecodeArgs
   const int64_t page_stride = (int64_t)p.hkv * head_stride;
   const int koff = col * kD + 8 * grp;
   const int voff = (lane >> 2) * kD + 16 * (lane & 3);
-  auto issue = [&](StepRegs& r, int pid_a, int pid_b) {
+  auto issue = [&](StepRegs& r, int pid_a, int pid_b) __attribute__((always_inline)) {
     const uint16_t* kb0 = p.k + pid_a * page_stride + g * head_stride;
     const uint16_t* vb0 = p.v + pid_a * page_stride + g * head_stride;
     const uint16_t* kb1 = p.k + pid_b * page_stride + g * head_stride;
@@ -145,7 +200,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(BalancedDecodeArgs
   // loaded before the K/V loads that precede its first use, so reading it
   // never waits for K/V data.
   int base = 0;
-  auto issue_step = [&](StepRegs& r, int st) {
+  auto issue_step = [&](StepRegs& r, int st) __attribute__((always_inline)) {
     const int j = min(st, n_steps - 1) - base;
     const int src = j < 32 ? ids : ids_next;
     const int jj = j & 31;
@@ -161,18 +216,159 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(BalancedDecodeArgs
   int b = m1 ? (63 - __clzll((long long)m1)) * stride : 0;
   if (stride > 1) b = find_request(p.page_indptr, B, p0, lane);
   b = __builtin_amdgcn_readfirstlane(b);
-  int seg_start = __builtin_amdgcn_readfirstlane(p.page_indptr[b]);
-  int seg_end = __builtin_amdgcn_readfirstlane(p.page_indptr[b + 1]);
-  int Lb = __builtin_amdgcn_readfirstlane(p.kv_len[b]);
+  int seg_start, seg_end, Lb;
+  // decode step: requests b .. b + 3 (lanes 16 r ..): page range and length,
+  // for the append below, in the same round trip (request b's from lane 0)
+  int g0_s0 = 0, g0_s1 = 0, g0_L = 0;
+  if constexpr (STEP) {
+    const int bb = b + (lane >> 4);
+    g0_s0 = bb < B ? p.page_indptr[bb] : p1;
+    g0_s1 = bb < B ? p.page_indptr[bb + 1] : p1;
+    g0_L = bb < B ? p.kv_len[bb] : 0;
+    seg_start = __builtin_amdgcn_readfirstlane(g0_s0);
+    seg_end = __builtin_amdgcn_readfirstlane(g0_s1);
+    Lb = __builtin_amdgcn_readfirstlane(g0_L);
+  } else {
+    seg_start = __builtin_amdgcn_readfirstlane(p.page_indptr[b]);
+    seg_end = __builtin_amdgcn_readfirstlane(p.page_indptr[b + 1]);
+    Lb = __builtin_amdgcn_readfirstlane(p.kv_len[b]);
+  }
 
   // Q^T operand of request bb (column `col` = head h; padding columns read
   // head g*G and are zeroed at use).
-  auto q_of = [&](int bb, u32x4& a, u32x4& c) {
+  auto q_of = [&](int bb, u32x4& a, u32x4& c) __attribute__((always_inline)) {
     const uint16_t* qh = p.q + ((int64_t)bb * p.hq + h) * kD + 8 * grp;
     a = ld16(qh);
     c = ld16(qh + 32);
   };
+
+  // Decode step.  Before it streams its range, the wave (1) appends the new
+  // keys and values whose cache slot lies in its pages -- it is the only
+  // reader of those slots -- and (2) rotates the query of every request its
+  // range holds into the query buffer (p.q) the decode reads; waves whose
+  // ranges share a request write the same values.  Requests go in groups of
+  // four.  Queries: lane (hs, j) = lane (lane / 8, lane % 8) takes piece j
+  // of query head g G + 8 hp + hs, for head passes hp; keys and values:
+  // sixteen lanes per request, eight for the key head and eight for the
+  // value head.  All of a group's loads go out before its arithmetic.  The
+  // stores complete (and are visible to this work-group's loads) before
+  // the queries are read and before any later step's loads are issued; the
+  // first step's, already in flight, are issued again when one of its two
+  // pages holds a new slot.
+  auto append_step = [&]() __attribute__((always_inline)) {
+    constexpr int kPasses = (G + 7) / 8;
+    const int j = lane & 7;
+    const int hs = lane >> 3;
+    const int off0 = p.interleaved ? 8 * j : 4 * j;
+    const int off1 = p.interleaved ? 8 * j + 4 : 32 + 4 * j;
+    const int64_t row_elems = (int64_t)(p.hq + 2 * p.hkv) * kD;
+    const u32x2 zero2 = {0u, 0u};
+    u32x2 qb0[kPasses], qb1[kPasses];   // query bias pieces (the same for every request)
+#pragma unroll
+    for (int hp = 0; hp < kPasses; ++hp) {
+      const int head = g * G + min(8 * hp + hs, G - 1);
+      qb0[hp] = p.bias != nullptr ? ld8(p.bias + (int64_t)head * kD + off0) : zero2;
+      qb1[hp] = p.bias != nullptr ? ld8(p.bias + (int64_t)head * kD + off1) : zero2;
+    }
+    const int rr = lane >> 4;           // key / value lanes: request bs + rr
+    const int role = (lane >> 3) & 1;   // 0: key head, 1: value head
+    const int kvhead = p.hq + role * p.hkv + g;
+    int first = p1;   // the first page of the range that receives a token
+    for (int bs = b; bs < B; bs += 4) {
+      const int bb = bs + rr;
+      const bool in = bb < B;
+      int s0 = g0_s0, s1 = g0_s1, L = g0_L;   // the first group's came with the lookup
+      if (bs != b) {
+        s0 = in ? p.page_indptr[bb] : p1;
+        s1 = in ? p.page_indptr[bb + 1] : p1;
+        L = in ? p.kv_len[bb] : 0;
+      }
+      if (__builtin_amdgcn_readfirstlane(s0) >= p1) break;   // request bs starts past the range
+      // queries: the group's requests that have pages in the range and a
+      // table row for their new token
+      bool qok[4];
+      int qpos[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rs0 = __builtin_amdgcn_readlane(s0, 16 * r);
+        const int rs1 = __builtin_amdgcn_readlane(s1, 16 * r);
+        const int rL = __builtin_amdgcn_readlane(L, 16 * r);
+        qok[r] = bs + r < B && rs0 < p1 && rs1 > p0 && rs1 > rs0 && rL >= 1 && rL <= p.max_pos;
+        qpos[r] = qok[r] ? rL - 1 : 0;
+      }
+      u32x2 qx0[4][kPasses], qx1[4][kPasses];
+      f32x4 qc[4], qs[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (!qok[r]) continue;
+        const float* cs = p.table + (int64_t)qpos[r] * kD + 4 * j;
+        qc[r] = *reinterpret_cast<const f32x4*>(cs);
+        qs[r] = *reinterpret_cast<const f32x4*>(cs + 32);
+#pragma unroll
+        for (int hp = 0; hp < kPasses; ++hp) {
+          const int head = g * G + min(8 * hp + hs, G - 1);
+          const uint16_t* src = p.qkv + (int64_t)(bs + r) * row_elems + (int64_t)head * kD;
+          qx0[r][hp] = ld8(src + off0);
+          qx1[r][hp] = ld8(src + off1);
+        }
+      }
+      // keys and values: lanes of request bb whose new slot is in the range
+      const int pos = L - 1;
+      const int pi = s0 + (pos >> 4);
+      const bool mine = in && L >= 1 && L <= p.max_pos && pi < s1 && pi >= p0 && pi < p1;
+      const uint64_t owners = __ballot(mine);
+      u32x2 kx0 = zero2, kx1 = zero2, kb0 = zero2, kb1 = zero2;
+      f32x4 kc = {0.f, 0.f, 0.f, 0.f}, ks = kc;
+      uint32_t page = 0;
+      if (mine) {
+        const uint16_t* src = p.qkv + (int64_t)bb * row_elems + (int64_t)kvhead * kD;
+        kx0 = ld8(src + off0);
+        kx1 = ld8(src + off1);
+        if (p.bias != nullptr) {
+          kb0 = ld8(p.bias + (int64_t)kvhead * kD + off0);
+          kb1 = ld8(p.bias + (int64_t)kvhead * kD + off1);
+        }
+        if (role == 0) {
+          const float* cs = p.table + (int64_t)pos * kD + 4 * j;
+          kc = *reinterpret_cast<const f32x4*>(cs);
+          ks = *reinterpret_cast<const f32x4*>(cs + 32);
+        }
+        page = (uint32_t)p.page_indices[pi];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (!qok[r]) continue;
+#pragma unroll
+        for (int hp = 0; hp < kPasses; ++hp) {
+          if (8 * hp + hs >= G) continue;
+          const int head = g * G + 8 * hp + hs;
+          new_piece(qx0[r][hp], qx1[r][hp], qb0[hp], qb1[hp], true, qc[r], qs[r], p.interleaved,
+                    p.q_new + ((int64_t)(bs + r) * p.hq + head) * kD, off0, off1);
+        }
+      }
+      if (owners != 0) {
+        // requests are in page order: the group's first owner has the lowest page
+        first = min(first, __builtin_amdgcn_readlane(pi, __builtin_ctzll(owners)));
+        if (mine)
+          new_piece(kx0, kx1, kb0, kb1, role == 0, kc, ks, p.interleaved,
+                    (role == 0 ? p.k_new : p.v_new) +
+                        (((int64_t)page * p.hkv + g) * kPage + (pos & (kPage - 1))) * kD,
+                    off0, off1);
+      }
+    }
+    wait_vmem<0>();
+    asm volatile("" ::: "memory");
+    first = __builtin_amdgcn_readfirstlane(first);
+    if (first < p0 + 2) issue_step(ra, 0);
+  };
+
   u32x4 qa, qc;
+  if constexpr (STEP) {
+    // the first step's loads are in flight while the new tokens are
+    // appended and the queries rotated (into the buffer q_of reads)
+    append_step();
+    __builtin_amdgcn_sched_barrier(0);
+  }
   q_of(b, qa, qc);
   settle(qa);
   settle(qc);
@@ -181,7 +377,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(BalancedDecodeArgs
   // pages costs no round trip.
   int nx_end, nx_L;
   u32x4 nqa, nqc;
-  auto prefetch_next = [&]() {
+  auto prefetch_next = [&]() __attribute__((always_inline)) {
     const int bn = min(b + 1, B - 1);
     nx_end = p.page_indptr[min(b + 2, B)];
     nx_L = p.kv_len[bn];
@@ -193,7 +389,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(BalancedDecodeArgs
   f32x4 o0, o1, o2, o3;
   // Online state in log2 units; a segment that holds its request's first
   // page starts at the sink (m = sigma log2 e, d = 1 on one lane group).
-  auto reset = [&](bool with_sink) {
+  auto reset = [&](bool with_sink) __attribute__((always_inline)) {
     m = with_sink ? sink * kLog2e : -INFINITY;
     d = (with_sink && grp == 0 && sink != -INFINITY) ? 1.f : 0.f;
     o0 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -204,7 +400,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(BalancedDecodeArgs
   uint16_t* my_v = lds_v + wave * kWaveLds;
 
   // Close the current segment (request b over this range's pages).
-  auto flush = [&]() {
+  auto flush = [&]() __attribute__((always_inline)) {
     float dt = d + xor_lane(d, 16);
     dt += xor_lane(dt, 32);
     const float inv = dt > 0.f ? 1.f / dt : 0.f;
@@ -246,7 +442,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(BalancedDecodeArgs
   // when the prefetch was issued within the same step, a lookup.  Either
   // branch leaves no load pending except the new prefetch, so the waits of
   // the step code never depend on which branch ran.
-  auto advance = [&](int pg, bool use_prefetch) {
+  auto advance = [&](int pg, bool use_prefetch) __attribute__((always_inline)) {
     const int ne = use_prefetch ? __builtin_amdgcn_readfirstlane(nx_end) : 0;
     if (use_prefetch && ne > seg_end) {
       b = b + 1;
@@ -272,7 +468,8 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(BalancedDecodeArgs
   // current request; use_a / use_b select the pages that belong to it.
   // na / nb: keys of page a / b that exist (the rest, and every key of a
   // page that is not used, are masked and their V rows zeroed).
-  auto process = [&](const StepRegs& r, int pa, bool use_a, bool use_b) {
+  auto process = [&](const StepRegs& r, int pa, bool use_a,
+                     bool use_b) __attribute__((always_inline)) {
     const int key_a = (pa - seg_start) * kPage;   // request position of page a's key 0
     const int na = use_a ? Lb - key_a : 0;
     const int nb = use_b ? Lb - key_a - kPage : 0;
@@ -335,7 +532,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(BalancedDecodeArgs
   // step's last page) and/or between the step's two pages (the step
   // straddles): each case is its own path, and only the first segment
   // change of a step uses the prefetch.
-  auto step_body = [&](const StepRegs& r, int pa) {
+  auto step_body = [&](const StepRegs& r, int pa) __attribute__((always_inline)) {
     // The next-request prefetch went out before the K/V loads of the other
     // register set, so completing it here waits for nothing this step's
     // own data does not already wait for.
@@ -477,18 +674,26 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(BalancedDecodeArgs p
 
 }  // namespace
 
-hipError_t launch_decode_balanced(const BalancedDecodeArgs& a, int group, hipStream_t stream) {
+namespace {
+template <bool STEP>
+hipError_t launch_first_pass(const BalancedDecodeArgs& a, int group, hipStream_t stream) {
   dim3 grid(a.n_ranges / kWaves, a.hkv);
   dim3 block(256);
   switch (group) {
-    case 1: hipLaunchKernelGGL(decode_balanced_kernel<1>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(decode_balanced_kernel<2>, grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(decode_balanced_kernel<4>, grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(decode_balanced_kernel<8>, grid, block, 0, stream, a); break;
-    case 16: hipLaunchKernelGGL(decode_balanced_kernel<16>, grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((decode_balanced_kernel<1, STEP>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_balanced_kernel<2, STEP>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_balanced_kernel<4, STEP>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_balanced_kernel<8, STEP>), grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((decode_balanced_kernel<16, STEP>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_decode_balanced(const BalancedDecodeArgs& a, int group, hipStream_t stream) {
+  return a.qkv != nullptr ? launch_first_pass<true>(a, group, stream)
+                          : launch_first_pass<false>(a, group, stream);
 }
 
 hipError_t launch_decode_finish(const BalancedDecodeArgs& a, hipStream_t stream) {

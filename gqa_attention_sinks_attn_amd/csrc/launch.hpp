@@ -44,6 +44,16 @@ struct BalancedDecodeArgs {
   float* lse;                   // [B, Hq] or nullptr
   float* o_part;                // [n_ranges + B - 1, Hq, 64]
   float* lse_part;              // [n_ranges + B - 1, Hq]
+  // Decode step (qkv != nullptr): the first pass also does the new token's
+  // bias, rotation and append; q then points at q_new.
+  const uint16_t* qkv;          // bf16 [B, Hq + 2 Hkv, 64], one new token per request
+  const uint16_t* bias;         // bf16 [(Hq + 2 Hkv) 64] or nullptr
+  const float* table;           // [max_pos, 64]: temperature x cos | temperature x sin
+  int32_t max_pos;
+  int32_t interleaved;          // 0: dim i pairs with i + 32; 1: 2i with 2i + 1
+  uint16_t* k_new;              // the K/V cache (k, v), written at each new token's slot
+  uint16_t* v_new;
+  uint16_t* q_new;              // bf16 [B, Hq, 64]: the rotated queries, written, then read as q
 };
 
 struct VerifyArgs {

@@ -70,9 +70,6 @@ __global__ __launch_bounds__(256) void rope_table_kernel(RopeTableArgs a) {
   a.table[(int64_t)p * kD + kHalf + d] = (float)(a.temperature * s);
 }
 
-__device__ __forceinline__ float lo_bf16(uint32_t w) { return bf16_bits_to_float(w & 0xffffu); }
-__device__ __forceinline__ float hi_bf16(uint32_t w) { return bf16_bits_to_float(w >> 16); }
-
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 // Per-token values every lane of the workgroup shares.
@@ -169,11 +166,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
     }
     if (rotated) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float uu = u[i], vv = v[i];
-        u[i] = uu * cv[r][i] - vv * sv[r][i];
-        v[i] = vv * cv[r][i] + uu * sv[r][i];
-      }
+      for (int i = 0; i < 4; ++i) rotate_pair(u[i], v[i], cv[r][i], sv[r][i]);
     }
     u32x2 o0, o1;
     if (a.interleaved) {

@@ -528,6 +528,55 @@ sink_attn_status sink_attn_qkv_rope_append(
     int32_t head_dim, int32_t page_size, int32_t total_q, int32_t interleaved,
     void* q_out, void* k_pages, void* v_pages, void* stream);
 
+/*
+ * sink_attn_decode_step: one decode step in one call -- each request's one
+ * new token gets its QKV bias and rotary encoding and is appended to the
+ * paged cache, and the decode then attends over the cache including it.
+ * The result (out, lse and the cache) equals, bit for bit,
+ *     sink_attn_qkv_rope_append(qkv, bias, rope_table, max_pos,
+ *         qo_indptr = 0, 1, .., batch, kv_len, page_indptr, page_indices,
+ *         batch, Hq, Hkv, 64, 16, total_q = batch, interleaved, q, k, v)
+ *     sink_attn_decode_balanced(q, k, v, page_indptr, page_indices, kv_len,
+ *         sinks, batch, Hq, Hkv, 64, 16, max_kv_len, num_ranges = 0, ...)
+ * but runs as two kernels instead of three: before it streams its pages,
+ * each wave of the decode's first pass appends the new keys and values of
+ * its own pages and rotates the queries of the requests it reads (into the
+ * workspace).
+ * GPT-OSS on Day 0, "Attention: GQA with attention sinks" (bias, YaRN) and
+ * "Sink attention"; Accelerating Sonar Through Speculation, "Inference with
+ * Speculative Decoding" (the new token's cache slot is reserved before the
+ * step).
+ *
+ *   qkv, bias        as sink_attn_qkv_rope_append, one row per request:
+ *                    bf16 [batch, Hq + 2 Hkv, 64]; bias may be NULL.
+ *   rope_table, max_pos, interleaved  as sink_attn_qkv_rope_append.
+ *   k_pages, v_pages the cache, read by the decode and written at each
+ *                    request's new slot: position p = kv_len[b] - 1, slot
+ *                    p % 16 of page page_indices[page_indptr[b] + p / 16].
+ *   kv_len           [batch]: keys of each request counting the new token.
+ *   the rest         as sink_attn_decode_balanced with num_ranges = 0.
+ *   workspace        sink_attn_decode_step_workspace_size() bytes: the
+ *                    balanced decode's partials, then the rotated queries
+ *                    (bf16 [batch, Hq, 64]).
+ * A request whose new position is not in [0, max_pos) is not written to the
+ * cache and its output is unspecified (its table row is read clamped);
+ * requests with kv_len = 0 get o = 0, lse = sink as in the decode.  Host
+ * checks as sink_attn_decode_balanced plus rope_table (non-NULL, 16-byte
+ * aligned), bias (16-byte aligned), max_pos >= 1, interleaved in {0, 1}
+ * and the workspace size.
+ */
+size_t sink_attn_decode_step_workspace_size(int32_t batch, int32_t num_qo_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t max_kv_len);
+sink_attn_status sink_attn_decode_step(
+    const void* qkv, const void* bias, const float* rope_table, int32_t max_pos,
+    int32_t interleaved, void* k_pages, void* v_pages,
+    const int32_t* page_indptr, const int32_t* page_indices, const int32_t* kv_len,
+    const float* sinks, int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t page_size, int32_t max_kv_len, float sm_scale,
+    void* out, sink_attn_dtype out_dtype, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* sink_attn_status_string(sink_attn_status s);
 

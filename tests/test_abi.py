@@ -488,3 +488,42 @@ def test_decode_noalloc_rejects_sizes_beyond_its_array():
     # the usual argument checks still come first for invalid sizes
     assert lib.sink_attn_decode_noalloc(None, A, A, A, A, A, A, 4, Hq, Hkv, 64, 16, 4096, 0, 0.125,
                                         A2, 1, None, None) == NULL
+
+
+def call_step(**over):
+    a = dict(qkv=A, bias=A, table=A, max_pos=4096, interleaved=0, k=A3, v=A3, page_indptr=A,
+             page_indices=A, kv_len=A, sinks=A, batch=4, hq=64, hkv=8, head_dim=64,
+             page_size=16, max_kv_len=4096, sm_scale=0.125, out=A2, out_dtype=1, lse=A3,
+             ws=A, ws_bytes=1 << 30, stream=0)
+    a.update(over)
+    return sa.lib().sink_attn_decode_step(
+        a["qkv"], a["bias"], a["table"], a["max_pos"], a["interleaved"], a["k"], a["v"],
+        a["page_indptr"], a["page_indices"], a["kv_len"], a["sinks"], a["batch"], a["hq"],
+        a["hkv"], a["head_dim"], a["page_size"], a["max_kv_len"], a["sm_scale"], a["out"],
+        a["out_dtype"], a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(qkv=None), NULL), (dict(table=None), NULL), (dict(k=None), NULL),
+    (dict(page_indices=None), NULL), (dict(out=None), NULL),
+    (dict(max_pos=0), SHAPE), (dict(batch=0), SHAPE), (dict(sm_scale=0.0), SHAPE),
+    (dict(interleaved=2), UNSUP), (dict(head_dim=128), UNSUP), (dict(page_size=32), UNSUP),
+    (dict(hq=24, hkv=8), UNSUP), (dict(hq=12, hkv=8), SHAPE), (dict(out_dtype=7), UNSUP),
+    (dict(bias=A + 2), MISAL), (dict(table=A + 4), MISAL), (dict(qkv=A + 8), MISAL),
+    (dict(k=A3 + 2), MISAL), (dict(out=A2 + 4), MISAL),
+    (dict(ws=None), WS), (dict(ws_bytes=16), WS),
+])
+def test_decode_step_validation(over, code):
+    assert call_step(**over) == code, sa.sink_attn_last_error()
+
+
+def test_decode_step_workspace_holds_the_queries():
+    """The step's workspace is the balanced decode's plus the rotated
+    queries (bf16 [batch, Hq, 64]); one byte less is refused."""
+    lib = sa.lib()
+    for B, Hq, Hkv, L in [(64, 64, 8, 4096), (3, 16, 1, 20), (256, 128, 8, 16384)]:
+        bal = lib.sink_attn_decode_balanced_workspace_size(B, Hq, Hkv, 64, L, 0)
+        step = lib.sink_attn_decode_step_workspace_size(B, Hq, Hkv, 64, L)
+        assert step >= bal + B * Hq * 64 * 2
+        assert step - bal < B * Hq * 64 * 2 + 256
+        assert call_step(batch=B, hq=Hq, hkv=Hkv, max_kv_len=L, ws_bytes=step - 1) == WS
