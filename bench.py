@@ -565,6 +565,34 @@ def append_lines(args, torch, sa, W, res, steps, warm):
                          achieved_gbs=round(alg / (ms * 1e-3) / 1e9, 1),
                          frac_hbm=round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          algorithmic_bytes=int(alg))
+        if name == "append_prefill_8x4096":
+            # the whole prefill step: append then attend, against the fused call
+            qlens = np.diff(ab.qo_indptr)
+            max_qlen, max_L = int(qlens.max()), int(ab.kv_len.max())
+            sinks = torch.from_numpy(
+                np.random.default_rng(1096).standard_normal(64).astype(np.float32)).cuda()
+            out = torch.empty((ab.total_q, 64, 64), dtype=torch.float32, device="cuda")
+            lse = torch.empty((ab.total_q, 64), dtype=torch.float32, device="cuda")
+
+            def pair(i):
+                call(i)
+                sa.sink_attn_prefill(q_out, qo, kp, vp, pi, px, kl, sinks, ab.batch, 64, 8, 64, 16,
+                                     ab.total_q, max_qlen, max_L, 0.125, 1, out, sa.F32, lse)
+
+            def fused(i):
+                sa.sink_attn_prefill_step(qkv, bias, table, 131072, 0, qo, kp, vp, pi, px, kl,
+                                          sinks, ab.batch, 64, 8, 64, 16, ab.total_q, max_qlen,
+                                          max_L, 0.125, 1, out, sa.F32, lse)
+            ms_pair = _time_calls(torch, pair, steps, warm)
+            ms_fused = _time_calls(torch, fused, steps, warm)
+            flops = sum(int(q) * (2 * int(L) - int(q) + 1) // 2 for q, L in zip(qlens, ab.kv_len)) \
+                * 64 * 4 * 64
+            res["prefill_step_8x4096"] = dict(
+                workload=f"prefill step: {ab.total_q} new tokens, 64q/8kv, d=64, page 16, YaRN",
+                call="sink_attn_qkv_rope_append + sink_attn_prefill, against sink_attn_prefill_step",
+                ms_pair=round(ms_pair, 5), ms_fused=round(ms_fused, 5),
+                tflops_fused=round(flops / (ms_fused * 1e-3) / 1e12, 2))
+            del out, lse
         del qkv, bias, kp, vp, q_out
         torch.cuda.empty_cache()
 

@@ -26,7 +26,7 @@ __all__ = [
     "sink_attn_decode_num_ranges", "sink_attn_verify", "sink_attn_verify_workspace_size",
     "sink_attn_verify_tree", "sink_attn_verify_num_splits", "sink_attn_rope_table",
     "sink_attn_qkv_rope_append", "sink_attn_decode_noalloc", "sink_attn_decode_step",
-    "sink_attn_decode_step_workspace_size",
+    "sink_attn_decode_step_workspace_size", "sink_attn_prefill_step",
     "sink_attn_status_string", "sink_attn_last_error", "sink_attn_version",
     "SYMBOLS",
 ]
@@ -42,7 +42,7 @@ SYMBOLS = (
     "sink_attn_decode_num_ranges", "sink_attn_verify", "sink_attn_verify_workspace_size",
     "sink_attn_verify_tree", "sink_attn_verify_num_splits", "sink_attn_rope_table",
     "sink_attn_qkv_rope_append", "sink_attn_decode_noalloc", "sink_attn_decode_step",
-    "sink_attn_decode_step_workspace_size",
+    "sink_attn_decode_step_workspace_size", "sink_attn_prefill_step",
     "sink_attn_status_string", "sink_attn_last_error", "sink_attn_version",
 )
 
@@ -122,6 +122,10 @@ def lib():
                                         _I, _I, _I, ctypes.c_float, _P, ctypes.c_int, _P, _P,
                                         ctypes.c_size_t, _P]
     L.sink_attn_decode_step.restype = ctypes.c_int
+    L.sink_attn_prefill_step.argtypes = [_P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I,
+                                         _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P,
+                                         ctypes.c_int, _P, _P]
+    L.sink_attn_prefill_step.restype = ctypes.c_int
     L.sink_attn_decode_step_workspace_size.argtypes = [_I, _I, _I, _I, _I]
     L.sink_attn_decode_step_workspace_size.restype = ctypes.c_size_t
     L.sink_attn_status_string.argtypes = [ctypes.c_int]
@@ -345,6 +349,20 @@ def sink_attn_rope_table(table, max_pos, head_dim, rope_theta, factor, original_
         _ptr(table), int(max_pos), int(head_dim), float(rope_theta), float(factor),
         int(original_max_pos), float(beta_fast), float(beta_slow), float(attn_factor),
         int(yarn_ramp), _stream(stream)))
+
+
+def sink_attn_prefill_step(qkv, bias, rope_table, max_pos, interleaved, qo_indptr, k_pages,
+                           v_pages, page_indptr, page_indices, kv_len, sinks, batch,
+                           num_qo_heads, num_kv_heads, head_dim, page_size, total_q, max_qlen,
+                           max_kv_len, sm_scale, causal, out, out_dtype, lse,
+                           stream=None) -> None:
+    _check(lib().sink_attn_prefill_step(
+        _ptr(qkv), _ptr(bias), _ptr(rope_table), int(max_pos), int(interleaved),
+        _ptr(qo_indptr), _ptr(k_pages), _ptr(v_pages), _ptr(page_indptr), _ptr(page_indices),
+        _ptr(kv_len), _ptr(sinks), int(batch), int(num_qo_heads), int(num_kv_heads),
+        int(head_dim), int(page_size), int(total_q), int(max_qlen), int(max_kv_len),
+        float(sm_scale), int(bool(causal)), _ptr(out), _dtype_code(out_dtype), _ptr(lse),
+        _stream(stream)))
 
 
 def sink_attn_decode_step_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim,

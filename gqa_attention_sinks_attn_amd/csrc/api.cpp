@@ -222,6 +222,102 @@ size_t sink_attn_decode_balanced_workspace_size(int32_t batch, int32_t num_qo_he
   return o_bytes + ((l_bytes + 255) / 256) * 256;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The queries of a prefill step: projection rows, bias, rotary table.
+struct PrefillStepInputs {
+  const void* qkv;
+  const void* bias;
+  const float* table;
+  int32_t max_pos;
+  int32_t interleaved;
+};
+
+// Host checks and launch arguments of a prefill (step == nullptr) or of a
+// prefill step's attention; nothing is launched.  *empty: no query rows.
+sink_attn_status prefill_check(const void* q, const int32_t* qo_indptr, const void* k,
+                               const void* v, const int32_t* kv_indptr,
+                               const int32_t* page_indices, const int32_t* kv_len,
+                               const float* sinks, int32_t batch, int32_t num_qo_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                               int32_t total_q, int32_t max_qlen, int32_t max_kv_len,
+                               float sm_scale, int32_t causal, void* out,
+                               sink_attn_dtype out_dtype, float* lse,
+                               const PrefillStepInputs* step, sa::PrefillArgs* a, bool* empty) {
+  const char* who = step ? "prefill_step" : "prefill";
+  const void* queries = step ? step->qkv : q;
+  if (!queries || !qo_indptr || !k || !v || !kv_indptr || !out)
+    return fail(SINK_ATTN_ERR_NULL_ARG, "%s: %s, qo_indptr, k, v, kv_indptr and out are required",
+                who, step ? "qkv" : "q");
+  if (page_indices && !kv_len)
+    return fail(SINK_ATTN_ERR_NULL_ARG, "%s: kv_len is required with a paged cache", who);
+  if (batch <= 0 || total_q < 0 || max_qlen < 0 || max_kv_len < 0)
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "%s: batch=%d total_q=%d max_qlen=%d max_kv_len=%d", who,
+                batch, total_q, max_qlen, max_kv_len);
+  if (max_qlen > total_q)
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "%s: max_qlen=%d exceeds total_q=%d", who, max_qlen,
+                total_q);
+  if (causal && max_qlen > 0 && max_kv_len <= 0)
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "%s: causal queries need keys (max_kv_len=%d)", who,
+                max_kv_len);
+  sink_attn_status st = check_heads(num_qo_heads, num_kv_heads);
+  if (st != SINK_ATTN_OK) return st;
+  if (head_dim != kHeadDim)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "%s: head_dim=%d (only 64 is built)", who, head_dim);
+  if (page_indices && page_size != kPageSize)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "%s: page_size=%d (only 16 is built)", who, page_size);
+  if (out_dtype != SINK_ATTN_BF16 && out_dtype != SINK_ATTN_F32)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "%s: unknown out_dtype %d", who, (int)out_dtype);
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "%s: sm_scale must be positive and finite", who);
+  if (!aligned(queries, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(SINK_ATTN_ERR_MISALIGNED, "%s: %s, k, v and out must be 16-byte aligned", who,
+                step ? "qkv" : "q");
+  if (!aligned(qo_indptr, 4) || !aligned(kv_indptr, 4) || (page_indices && !aligned(page_indices, 4)) ||
+      (kv_len && !aligned(kv_len, 4)) || (sinks && !aligned(sinks, 4)) || (lse && !aligned(lse, 4)))
+    return fail(SINK_ATTN_ERR_MISALIGNED, "%s: index, sink and lse arrays must be 4-byte aligned",
+                who);
+  *empty = total_q == 0 || max_qlen == 0;
+  if (*empty) return ok();
+  {
+    // one workgroup per (256 / G query tokens, KV head, request): a flat grid
+    const int64_t tokens_per_wg = 256 / (num_qo_heads / num_kv_heads);
+    const int64_t wgs = (max_qlen + tokens_per_wg - 1) / tokens_per_wg * num_kv_heads * (int64_t)batch;
+    if (wgs > 0x7fffffff)
+      return fail(SINK_ATTN_ERR_BAD_SHAPE, "%s: %lld workgroups exceed the grid limit", who,
+                  (long long)wgs);
+  }
+  a->q = static_cast<const uint16_t*>(q);
+  a->qo_indptr = qo_indptr;
+  a->k = static_cast<const uint16_t*>(k);
+  a->v = static_cast<const uint16_t*>(v);
+  a->kv_indptr = kv_indptr;
+  a->page_indices = page_indices;
+  a->kv_len = kv_len;
+  a->sinks = sinks;
+  a->batch = batch;
+  a->hq = num_qo_heads;
+  a->hkv = num_kv_heads;
+  a->max_qlen = max_qlen;
+  a->causal = causal ? 1 : 0;
+  a->scale_log2 = sm_scale * 1.4426950408889634f;
+  a->out = out;
+  a->out_f32 = out_dtype == SINK_ATTN_F32;
+  a->lse = lse;
+  a->qkv = step ? static_cast<const uint16_t*>(step->qkv) : nullptr;
+  a->bias = step ? static_cast<const uint16_t*>(step->bias) : nullptr;
+  a->table = step ? step->table : nullptr;
+  a->max_pos = step ? step->max_pos : 0;
+  a->interleaved = step ? step->interleaved : 0;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 sink_attn_status sink_attn_prefill(const void* q, const int32_t* qo_indptr, const void* k,
                                    const void* v, const int32_t* kv_indptr,
                                    const int32_t* page_indices, const int32_t* kv_len,
@@ -230,60 +326,13 @@ sink_attn_status sink_attn_prefill(const void* q, const int32_t* qo_indptr, cons
                                    int32_t total_q, int32_t max_qlen, int32_t max_kv_len,
                                    float sm_scale, int32_t causal, void* out,
                                    sink_attn_dtype out_dtype, float* lse, void* stream) {
-  if (!q || !qo_indptr || !k || !v || !kv_indptr || !out)
-    return fail(SINK_ATTN_ERR_NULL_ARG, "prefill: q, qo_indptr, k, v, kv_indptr and out are required");
-  if (page_indices && !kv_len)
-    return fail(SINK_ATTN_ERR_NULL_ARG, "prefill: kv_len is required with a paged cache");
-  if (batch <= 0 || total_q < 0 || max_qlen < 0 || max_kv_len < 0)
-    return fail(SINK_ATTN_ERR_BAD_SHAPE, "prefill: batch=%d total_q=%d max_qlen=%d max_kv_len=%d",
-                batch, total_q, max_qlen, max_kv_len);
-  if (max_qlen > total_q)
-    return fail(SINK_ATTN_ERR_BAD_SHAPE, "prefill: max_qlen=%d exceeds total_q=%d", max_qlen, total_q);
-  if (causal && max_qlen > 0 && max_kv_len <= 0)
-    return fail(SINK_ATTN_ERR_BAD_SHAPE, "prefill: causal queries need keys (max_kv_len=%d)", max_kv_len);
-  sink_attn_status st = check_heads(num_qo_heads, num_kv_heads);
-  if (st != SINK_ATTN_OK) return st;
-  if (head_dim != kHeadDim)
-    return fail(SINK_ATTN_ERR_UNSUPPORTED, "prefill: head_dim=%d (only 64 is built)", head_dim);
-  if (page_indices && page_size != kPageSize)
-    return fail(SINK_ATTN_ERR_UNSUPPORTED, "prefill: page_size=%d (only 16 is built)", page_size);
-  if (out_dtype != SINK_ATTN_BF16 && out_dtype != SINK_ATTN_F32)
-    return fail(SINK_ATTN_ERR_UNSUPPORTED, "prefill: unknown out_dtype %d", (int)out_dtype);
-  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
-    return fail(SINK_ATTN_ERR_BAD_SHAPE, "prefill: sm_scale must be positive and finite");
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
-    return fail(SINK_ATTN_ERR_MISALIGNED, "prefill: q, k, v and out must be 16-byte aligned");
-  if (!aligned(qo_indptr, 4) || !aligned(kv_indptr, 4) || (page_indices && !aligned(page_indices, 4)) ||
-      (kv_len && !aligned(kv_len, 4)) || (sinks && !aligned(sinks, 4)) || (lse && !aligned(lse, 4)))
-    return fail(SINK_ATTN_ERR_MISALIGNED, "prefill: index, sink and lse arrays must be 4-byte aligned");
-  if (total_q == 0 || max_qlen == 0) return ok();
-  {
-    // one workgroup per (256 / G query tokens, KV head, request): a flat grid
-    const int64_t tokens_per_wg = 256 / (num_qo_heads / num_kv_heads);
-    const int64_t wgs = (max_qlen + tokens_per_wg - 1) / tokens_per_wg * num_kv_heads * (int64_t)batch;
-    if (wgs > 0x7fffffff)
-      return fail(SINK_ATTN_ERR_BAD_SHAPE, "prefill: %lld workgroups exceed the grid limit",
-                  (long long)wgs);
-  }
-
   sa::PrefillArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.qo_indptr = qo_indptr;
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.kv_indptr = kv_indptr;
-  a.page_indices = page_indices;
-  a.kv_len = kv_len;
-  a.sinks = sinks;
-  a.batch = batch;
-  a.hq = num_qo_heads;
-  a.hkv = num_kv_heads;
-  a.max_qlen = max_qlen;
-  a.causal = causal ? 1 : 0;
-  a.scale_log2 = sm_scale * 1.4426950408889634f;
-  a.out = out;
-  a.out_f32 = out_dtype == SINK_ATTN_F32;
-  a.lse = lse;
+  bool empty = false;
+  sink_attn_status st = prefill_check(q, qo_indptr, k, v, kv_indptr, page_indices, kv_len, sinks,
+                                      batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                      total_q, max_qlen, max_kv_len, sm_scale, causal, out,
+                                      out_dtype, lse, nullptr, &a, &empty);
+  if (st != SINK_ATTN_OK || empty) return st;
   return hip_status(sa::launch_prefill(a, num_qo_heads / num_kv_heads,
                                        static_cast<hipStream_t>(stream)),
                     "prefill launch");
@@ -1006,6 +1055,63 @@ sink_attn_status sink_attn_rope_table(float* table, int32_t max_pos, int32_t hea
   return hip_status(sa::launch_rope_table(a, static_cast<hipStream_t>(stream)), "rope_table launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Host checks and launch arguments of the append (kv_only: the key and
+// value heads only, q_out unused); nothing is launched.
+sink_attn_status append_check(const void* qkv, const void* bias, const float* rope_table,
+                              int32_t max_pos, const int32_t* qo_indptr, const int32_t* kv_len,
+                              const int32_t* page_indptr, const int32_t* page_indices,
+                              int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t page_size, int32_t total_q,
+                              int32_t interleaved, void* q_out, void* k_pages, void* v_pages,
+                              int32_t kv_only, sa::RopeAppendArgs* a) {
+  const char* who = kv_only ? "prefill_step" : "qkv_rope_append";
+  if (!qkv || !rope_table || !qo_indptr || !kv_len || !page_indptr || !page_indices ||
+      (!q_out && !kv_only) || !k_pages || !v_pages)
+    return fail(SINK_ATTN_ERR_NULL_ARG, "%s: only bias may be NULL", who);
+  if (batch < 1 || num_qo_heads < 1 || num_kv_heads < 1 || total_q < 0 || max_pos < 1)
+    return fail(SINK_ATTN_ERR_BAD_SHAPE, "%s: batch=%d Hq=%d Hkv=%d total_q=%d max_pos=%d", who,
+                batch, num_qo_heads, num_kv_heads, total_q, max_pos);
+  if (head_dim != kHeadDim || page_size != kPageSize)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "%s: head_dim %d, page_size %d (only 64, 16)", who,
+                head_dim, page_size);
+  if (interleaved != 0 && interleaved != 1)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "%s: interleaved must be 0 or 1", who);
+  if ((int64_t)total_q * 256 > 0xFFFFFFFFll || num_qo_heads + 2 * num_kv_heads > 65535 * 32)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "%s: grid too large", who);
+  if (!aligned(qkv, 16) || (bias && !aligned(bias, 16)) || !aligned(rope_table, 16) ||
+      (q_out && !aligned(q_out, 16)) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
+      !aligned(qo_indptr, 4) || !aligned(kv_len, 4) || !aligned(page_indptr, 4) ||
+      !aligned(page_indices, 4))
+    return fail(SINK_ATTN_ERR_MISALIGNED,
+                "%s: tensors must be 16-byte, index arrays 4-byte aligned", who);
+  a->qkv = static_cast<const uint16_t*>(qkv);
+  a->bias = static_cast<const uint16_t*>(bias);
+  a->table = rope_table;
+  a->max_pos = max_pos;
+  a->qo_indptr = qo_indptr;
+  a->kv_len = kv_len;
+  a->page_indptr = page_indptr;
+  a->page_indices = page_indices;
+  a->batch = batch;
+  a->hq = num_qo_heads;
+  a->hkv = num_kv_heads;
+  a->total_q = total_q;
+  a->interleaved = interleaved;
+  a->kv_only = kv_only;
+  a->q_out = static_cast<uint16_t*>(q_out);
+  a->k_pages = static_cast<uint16_t*>(k_pages);
+  a->v_pages = static_cast<uint16_t*>(v_pages);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 sink_attn_status sink_attn_qkv_rope_append(const void* qkv, const void* bias,
                                            const float* rope_table, int32_t max_pos,
                                            const int32_t* qo_indptr, const int32_t* kv_len,
@@ -1015,45 +1121,44 @@ sink_attn_status sink_attn_qkv_rope_append(const void* qkv, const void* bias,
                                            int32_t head_dim, int32_t page_size, int32_t total_q,
                                            int32_t interleaved, void* q_out, void* k_pages,
                                            void* v_pages, void* stream) {
-  if (!qkv || !rope_table || !qo_indptr || !kv_len || !page_indptr || !page_indices || !q_out ||
-      !k_pages || !v_pages)
-    return fail(SINK_ATTN_ERR_NULL_ARG, "qkv_rope_append: only bias may be NULL");
-  if (batch < 1 || num_qo_heads < 1 || num_kv_heads < 1 || total_q < 0 || max_pos < 1)
-    return fail(SINK_ATTN_ERR_BAD_SHAPE, "qkv_rope_append: batch=%d Hq=%d Hkv=%d total_q=%d max_pos=%d",
-                batch, num_qo_heads, num_kv_heads, total_q, max_pos);
-  if (head_dim != kHeadDim || page_size != kPageSize)
-    return fail(SINK_ATTN_ERR_UNSUPPORTED, "qkv_rope_append: head_dim %d, page_size %d (only 64, 16)",
-                head_dim, page_size);
-  if (interleaved != 0 && interleaved != 1)
-    return fail(SINK_ATTN_ERR_UNSUPPORTED, "qkv_rope_append: interleaved must be 0 or 1");
-  if ((int64_t)total_q * 256 > 0xFFFFFFFFll || num_qo_heads + 2 * num_kv_heads > 65535 * 32)
-    return fail(SINK_ATTN_ERR_UNSUPPORTED, "qkv_rope_append: grid too large");
-  if (!aligned(qkv, 16) || (bias && !aligned(bias, 16)) || !aligned(rope_table, 16) ||
-      !aligned(q_out, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
-      !aligned(qo_indptr, 4) || !aligned(kv_len, 4) || !aligned(page_indptr, 4) ||
-      !aligned(page_indices, 4))
-    return fail(SINK_ATTN_ERR_MISALIGNED,
-                "qkv_rope_append: tensors must be 16-byte, index arrays 4-byte aligned");
-  if (total_q == 0) return ok();
   sa::RopeAppendArgs a;
-  a.qkv = static_cast<const uint16_t*>(qkv);
-  a.bias = static_cast<const uint16_t*>(bias);
-  a.table = rope_table;
-  a.max_pos = max_pos;
-  a.qo_indptr = qo_indptr;
-  a.kv_len = kv_len;
-  a.page_indptr = page_indptr;
-  a.page_indices = page_indices;
-  a.batch = batch;
-  a.hq = num_qo_heads;
-  a.hkv = num_kv_heads;
-  a.total_q = total_q;
-  a.interleaved = interleaved;
-  a.q_out = static_cast<uint16_t*>(q_out);
-  a.k_pages = static_cast<uint16_t*>(k_pages);
-  a.v_pages = static_cast<uint16_t*>(v_pages);
+  sink_attn_status st = append_check(qkv, bias, rope_table, max_pos, qo_indptr, kv_len,
+                                     page_indptr, page_indices, batch, num_qo_heads,
+                                     num_kv_heads, head_dim, page_size, total_q, interleaved,
+                                     q_out, k_pages, v_pages, 0, &a);
+  if (st != SINK_ATTN_OK || total_q == 0) return st;
   return hip_status(sa::launch_rope_append(a, static_cast<hipStream_t>(stream)),
                     "qkv_rope_append launch");
+}
+
+sink_attn_status sink_attn_prefill_step(
+    const void* qkv, const void* bias, const float* rope_table, int32_t max_pos,
+    int32_t interleaved, const int32_t* qo_indptr, void* k_pages, void* v_pages,
+    const int32_t* page_indptr, const int32_t* page_indices, const int32_t* kv_len,
+    const float* sinks, int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t page_size, int32_t total_q, int32_t max_qlen, int32_t max_kv_len,
+    float sm_scale, int32_t causal, void* out, sink_attn_dtype out_dtype, float* lse,
+    void* stream) {
+  // every check of both kernels before either is launched
+  sa::RopeAppendArgs ap;
+  sink_attn_status st = append_check(qkv, bias, rope_table, max_pos, qo_indptr, kv_len,
+                                     page_indptr, page_indices, batch, num_qo_heads,
+                                     num_kv_heads, head_dim, page_size, total_q, interleaved,
+                                     nullptr, k_pages, v_pages, 1, &ap);
+  if (st != SINK_ATTN_OK) return st;
+  const PrefillStepInputs step = {qkv, bias, rope_table, max_pos, interleaved};
+  sa::PrefillArgs a;
+  bool empty = false;
+  st = prefill_check(nullptr, qo_indptr, k_pages, v_pages, page_indptr, page_indices, kv_len,
+                     sinks, batch, num_qo_heads, num_kv_heads, head_dim, page_size, total_q,
+                     max_qlen, max_kv_len, sm_scale, causal, out, out_dtype, lse, &step, &a,
+                     &empty);
+  if (st != SINK_ATTN_OK || total_q == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(sa::launch_rope_append(ap, s), "prefill_step append launch");
+  if (st != SINK_ATTN_OK || empty) return st;
+  return hip_status(sa::launch_prefill(a, num_qo_heads / num_kv_heads, s),
+                    "prefill_step launch");
 }
 
 }  // extern "C"

@@ -127,6 +127,13 @@ struct PrefillArgs {
   void* out;
   int32_t out_f32;
   float* lse;
+  // Prefill step (qkv != nullptr, paged cache): the queries are read from
+  // the projection rows and biased and rotated at load; q is unused.
+  const uint16_t* qkv;          // bf16 [total_q, Hq + 2 Hkv, 64]
+  const uint16_t* bias;         // bf16 [(Hq + 2 Hkv) 64] or nullptr
+  const float* table;           // [max_pos, 64]
+  int32_t max_pos;
+  int32_t interleaved;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
@@ -151,6 +158,7 @@ struct RopeAppendArgs {
   const int32_t* page_indptr;   // [B+1]
   const int32_t* page_indices;
   int32_t batch, hq, hkv, total_q, interleaved;
+  int32_t kv_only;              // 1: the key and value heads only (q_out unused)
   uint16_t* q_out;              // bf16 [total_q, Hq, 64]
   uint16_t* k_pages;            // bf16 [num_pages, Hkv, 16, 64]
   uint16_t* v_pages;

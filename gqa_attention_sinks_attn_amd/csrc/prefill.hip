@@ -52,7 +52,7 @@ constexpr int kTileBytes = kTile * kD * 2;  // one K or V tile in LDS, rows unpa
 constexpr int kBufs = 3;                    // LDS tile buffers
 constexpr float kFastLimit = 65536.f; // row tile sum that forces a rescale
 
-template <int G, bool PAGED>
+template <int G, bool PAGED, bool STEP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs p) {
   constexpr int T = 256 / G;  // tokens per workgroup
   __shared__ __attribute__((aligned(1024))) char lds_k[kBufs * kTileBytes];
@@ -113,11 +113,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     pos[cb] = valid[cb] ? pos_base + tok[cb] : -1;
     const int last_tok = min(t0 + tl_last, qlen - 1);
     wave_pos_max = max(wave_pos_max, pos_base + last_tok);
-    const uint16_t* qrow =
-        p.q + ((int64_t)(q_begin + (valid[cb] ? tok[cb] : 0)) * p.hq + head[cb]) * kD + 8 * hh;
     const u32x4 z = {0u, 0u, 0u, 0u};
+    if constexpr (STEP) {
+      // The query from its projection row: bias added in fp32, rotated by
+      // the token's table row with the append kernel's arithmetic, rounded
+      // to bf16 once.  The lane holds dims 8 hh + 16 s .. + 7 (s = 0..3),
+      // so both members of every rotated pair: dims d and d + 32 (chunks s
+      // and s + 2) in the rotate-half pairing, 2 i and 2 i + 1 (inside a
+      // chunk) interleaved.  A position outside the table is read clamped
+      // (the append writes nothing for it; the row's result is unspecified).
+      const int row = q_begin + (valid[cb] ? tok[cb] : 0);
+      const uint16_t* xrow = p.qkv + ((int64_t)row * (p.hq + 2 * p.hkv) + head[cb]) * kD + 8 * hh;
+      const float* trow = p.table + (int64_t)min(max(pos[cb], 0), p.max_pos - 1) * kD;
+      float x[4][8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) bq[cb][s] = as_bf16x8(valid[cb] ? ld16(qrow + 16 * s) : z);
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 w = ld16(xrow + 16 * s);
+        const u32x4 bw = p.bias != nullptr ? ld16(p.bias + (int64_t)head[cb] * kD + 8 * hh + 16 * s) : z;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[s][2 * i] = lo_bf16(w[i]) + lo_bf16(bw[i]);
+          x[s][2 * i + 1] = hi_bf16(w[i]) + hi_bf16(bw[i]);
+        }
+      }
+      if (p.interleaved) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const f32x4 c = *reinterpret_cast<const f32x4*>(trow + 8 * s + 4 * hh);
+          const f32x4 sn = *reinterpret_cast<const f32x4*>(trow + 32 + 8 * s + 4 * hh);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) rotate_pair(x[s][2 * k], x[s][2 * k + 1], c[k], sn[k]);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const float* cs = trow + 16 * s + 8 * hh;
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs);
+          const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + 4);
+          const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs + 32);
+          const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + 36);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            rotate_pair(x[s][i], x[s + 2][i], i < 4 ? c0[i] : c1[i - 4], i < 4 ? s0[i] : s1[i - 4]);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 y = {pack_bf16x2(x[s][0], x[s][1]), pack_bf16x2(x[s][2], x[s][3]),
+                         pack_bf16x2(x[s][4], x[s][5]), pack_bf16x2(x[s][6], x[s][7])};
+        bq[cb][s] = as_bf16x8(valid[cb] ? y : z);
+      }
+    } else {
+      const uint16_t* qrow =
+          p.q + ((int64_t)(q_begin + (valid[cb] ? tok[cb] : 0)) * p.hq + head[cb]) * kD + 8 * hh;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) bq[cb][s] = as_bf16x8(valid[cb] ? ld16(qrow + 16 * s) : z);
+    }
   }
 
   // ---- key range of the workgroup ----
@@ -500,10 +551,12 @@ hipError_t launch_g(const PrefillArgs& a, hipStream_t stream) {
   const int64_t wgs = (int64_t)q_tiles * a.hkv * a.batch;
   if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)wgs);
-  if (a.page_indices != nullptr)
-    hipLaunchKernelGGL((prefill_kernel<G, true>), grid, dim3(256), 0, stream, a);
+  if (a.qkv != nullptr)   // the prefill step: a paged cache
+    hipLaunchKernelGGL((prefill_kernel<G, true, true>), grid, dim3(256), 0, stream, a);
+  else if (a.page_indices != nullptr)
+    hipLaunchKernelGGL((prefill_kernel<G, true, false>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<G, false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<G, false, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

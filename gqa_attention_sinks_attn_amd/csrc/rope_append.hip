@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
   }
 
   const int H = a.hq + 2 * a.hkv;
-  const int h = block_y() * kHeadsPerBlock + (thread_x() >> 3);
+  const int h = (a.kv_only ? a.hq : 0) + block_y() * kHeadsPerBlock + (thread_x() >> 3);
   if (h >= H) return;
   const int j = thread_x() & 7;
   const bool rotated = h < a.hq + a.hkv;
@@ -194,7 +194,7 @@ hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t stream) {
-  const int H = a.hq + 2 * a.hkv;
+  const int H = a.kv_only ? 2 * a.hkv : a.hq + 2 * a.hkv;
   dim3 grid((unsigned)((a.total_q + kRowsPerBlock - 1) / kRowsPerBlock),
             (unsigned)((H + kHeadsPerBlock - 1) / kHeadsPerBlock));
   hipLaunchKernelGGL(rope_append_kernel, grid, dim3(256), 0, stream, a);

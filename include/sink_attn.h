@@ -529,6 +529,44 @@ sink_attn_status sink_attn_qkv_rope_append(
     void* q_out, void* k_pages, void* v_pages, void* stream);
 
 /*
+ * sink_attn_prefill_step: one prefill (or chunked-prefill, or verification)
+ * step in one call -- the new tokens' QKV bias and rotary encoding, the
+ * append of their keys and values to the paged cache, and the causal (or
+ * full) attention of their queries over the cache.  The result (out, lse
+ * and the cache) equals, bit for bit,
+ *     sink_attn_qkv_rope_append(qkv, bias, rope_table, max_pos, qo_indptr,
+ *         kv_len, page_indptr, page_indices, batch, Hq, Hkv, 64, 16,
+ *         total_q, interleaved, q, k, v)
+ *     sink_attn_prefill(q, qo_indptr, k, v, page_indptr, page_indices,
+ *         kv_len, sinks, batch, Hq, Hkv, 64, 16, total_q, max_qlen,
+ *         max_kv_len, sm_scale, causal, out, out_dtype, lse)
+ * but the rotated queries are never written out: the append writes the key
+ * and value heads only, and the attention kernel reads each query from its
+ * projection row, adding the bias and rotating it as it loads it.  GPT-OSS
+ * on Day 0, "Attention: GQA with attention sinks" (bias, YaRN) and "Sink
+ * attention"; Accelerating Sonar Through Speculation, "Inference with
+ * Speculative Decoding" (the new tokens' cache slots are reserved before
+ * the step).
+ *
+ *   qkv, bias, rope_table, max_pos, interleaved  as sink_attn_qkv_rope_append.
+ *   qo_indptr, kv_len, page_indptr, page_indices  as both calls above (a
+ *                    paged cache; kv_len counts the new tokens).
+ *   k_pages, v_pages the cache, written at the new tokens' slots and read.
+ *   the rest         as sink_attn_prefill.
+ * A token whose position is not in [0, max_pos) is not appended and its
+ * row's result is unspecified.  Host checks: those of both calls, before
+ * either kernel is launched.
+ */
+sink_attn_status sink_attn_prefill_step(
+    const void* qkv, const void* bias, const float* rope_table, int32_t max_pos,
+    int32_t interleaved, const int32_t* qo_indptr, void* k_pages, void* v_pages,
+    const int32_t* page_indptr, const int32_t* page_indices, const int32_t* kv_len,
+    const float* sinks, int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t page_size, int32_t total_q, int32_t max_qlen,
+    int32_t max_kv_len, float sm_scale, int32_t causal,
+    void* out, sink_attn_dtype out_dtype, float* lse, void* stream);
+
+/*
  * sink_attn_decode_step: one decode step in one call -- each request's one
  * new token gets its QKV bias and rotary encoding and is appended to the
  * paged cache, and the decode then attends over the cache including it.

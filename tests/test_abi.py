@@ -527,3 +527,35 @@ def test_decode_step_workspace_holds_the_queries():
         assert step >= bal + B * Hq * 64 * 2
         assert step - bal < B * Hq * 64 * 2 + 256
         assert call_step(batch=B, hq=Hq, hkv=Hkv, max_kv_len=L, ws_bytes=step - 1) == WS
+
+
+def call_prefill_step(**over):
+    a = dict(qkv=A, bias=A, table=A, max_pos=4096, interleaved=0, qo=A, k=A3, v=A3,
+             page_indptr=A, page_indices=A, kv_len=A, sinks=A, batch=4, hq=64, hkv=8,
+             head_dim=64, page_size=16, total_q=40, max_qlen=10, max_kv_len=4096,
+             sm_scale=0.125, causal=1, out=A2, out_dtype=1, lse=A3, stream=0)
+    a.update(over)
+    return sa.lib().sink_attn_prefill_step(
+        a["qkv"], a["bias"], a["table"], a["max_pos"], a["interleaved"], a["qo"], a["k"], a["v"],
+        a["page_indptr"], a["page_indices"], a["kv_len"], a["sinks"], a["batch"], a["hq"],
+        a["hkv"], a["head_dim"], a["page_size"], a["total_q"], a["max_qlen"], a["max_kv_len"],
+        a["sm_scale"], a["causal"], a["out"], a["out_dtype"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(qkv=None), NULL), (dict(table=None), NULL), (dict(page_indices=None), NULL),
+    (dict(kv_len=None), NULL), (dict(k=None), NULL), (dict(out=None), NULL),
+    (dict(qo=None), NULL),
+    (dict(max_pos=0), SHAPE), (dict(batch=0), SHAPE), (dict(max_qlen=50), SHAPE),
+    (dict(sm_scale=-1.0), SHAPE), (dict(hq=12, hkv=8), SHAPE),
+    (dict(interleaved=3), UNSUP), (dict(head_dim=32), UNSUP), (dict(page_size=8), UNSUP),
+    (dict(hq=24, hkv=8), UNSUP), (dict(out_dtype=5), UNSUP),
+    (dict(bias=A + 2), MISAL), (dict(table=A + 4), MISAL), (dict(qkv=A + 8), MISAL),
+    (dict(k=A3 + 2), MISAL), (dict(out=A2 + 8), MISAL), (dict(lse=A3 + 2), MISAL),
+])
+def test_prefill_step_validation(over, code):
+    assert call_prefill_step(**over) == code, sa.sink_attn_last_error()
+
+
+def test_prefill_step_with_no_rows_launches_nothing():
+    assert call_prefill_step(total_q=0, max_qlen=0) == OK
