@@ -62,11 +62,11 @@ CSRC = os.path.join(ROOT, "gqa_attention_sinks_attn_amd", "csrc")
 # kernel and by the hash of the sources that build it.  A source change
 # makes the figure stale: it is then reported as null until retaken.
 TRAFFIC = {
-    "c2": (260_943_357, "decode_balanced.hip", "9a447f3f65222092"),
-    "c3": (1_076_443_896, "decode_balanced.hip", "9a447f3f65222092"),
-    "c4": (1_876_166_305, "prefill.hip", "4505943ee4bbf007"),
-    "c5_prefill": (6_378_097_745, "prefill.hip", "4505943ee4bbf007"),
-    "c5_decode": (4_355_372_852, "decode_balanced.hip", "9a447f3f65222092"),
+    "c2": (260_938_798, "decode_balanced.hip", "9a447f3f65222092"),
+    "c3": (1_076_430_655, "decode_balanced.hip", "9a447f3f65222092"),
+    "c4": (1_876_238_689, "prefill.hip", "414b58e2ad11b37b"),
+    "c5_prefill": (6_376_976_874, "prefill.hip", "414b58e2ad11b37b"),
+    "c5_decode": (4_355_406_703, "decode_balanced.hip", "9a447f3f65222092"),
 }
 
 
