@@ -290,3 +290,79 @@ def test_verify_random_drafts_match_the_oracle(c):
     out, lse, bf16 = gpu(b, plan="verify")
     ref, rl = oracle.attend(b)
     check(f"property verify tree={c['tree']}", out, ref, lse, rl, bf16_out=bf16)
+
+
+# ------------------------------------------------------------ the fused steps
+
+STEP_MAX_POS = 4096
+
+
+@pytest.fixture(scope="module")
+def rope_table():
+    from gqa_attention_sinks_attn_amd import sink_attn_rope_table
+    t = torch.empty((STEP_MAX_POS, 64), dtype=torch.float32, device="cuda")
+    sink_attn_rope_table(t, STEP_MAX_POS, 64, 150000.0, 32.0, 4096, 32.0, 1.0, 0.0)
+    torch.cuda.synchronize()
+    return t
+
+
+def sink_values(kind, hq, rng):
+    s, std = sinks_arg(kind)
+    if s is None:
+        return None
+    if isinstance(s, str):
+        return (std * rng.standard_normal(hq)).astype(np.float32)
+    return np.full(hq, s, np.float32)
+
+
+@st.composite
+def step_cases(draw, decode):
+    hq, hkv = draw(st.sampled_from(GROUPS))
+    B = draw(st.integers(1, 12 if decode else 4))
+    if decode:
+        qlens = [1] * B
+        kv_lens = draw(st.lists(st.integers(1, 600), min_size=B, max_size=B))
+    else:
+        qlens = draw(st.lists(st.integers(1, 80), min_size=B, max_size=B))
+        prefix = draw(st.lists(st.integers(0, 200), min_size=B, max_size=B))
+        kv_lens = [p + q for p, q in zip(prefix, qlens)]
+    return dict(hq=hq, hkv=hkv, qlens=qlens, kv_lens=kv_lens,
+                interleaved=draw(st.sampled_from([0, 1])), bias=draw(st.booleans()),
+                spare=draw(st.integers(0, 4)), sinks=draw(SINKS),
+                out=draw(st.sampled_from(["f32", "bf16"])),
+                causal=True if decode else draw(st.booleans()),
+                seed=draw(st.integers(0, 2**31 - 1)))
+
+
+def step_inputs(c):
+    rng = np.random.default_rng(c["seed"])
+    ab = W.make_append_batch(rng, qlens=c["qlens"], kv_lens=c["kv_lens"], hq=c["hq"],
+                             hkv=c["hkv"], bias=c["bias"], spare_pages=c["spare"])
+    od = torch.float32 if c["out"] == "f32" else torch.bfloat16
+    return ab, sink_values(c["sinks"], c["hq"], rng), od
+
+
+@SETTINGS
+@given(c=step_cases(decode=True))
+def test_decode_step_is_the_append_then_the_decode(rope_table, c):
+    """sink_attn_decode_step against sink_attn_qkv_rope_append followed by
+    sink_attn_decode_balanced: output, LSE and the whole cache bit for bit."""
+    from tests import test_gpu_decode_step as DS
+    say(f"[case] decode step {c}")
+    ab, sinks, od = step_inputs(c)
+    res = DS.run_both(ab, rope_table, sinks, c["interleaved"], out_dtype=od, bias=c["bias"],
+                      max_pos=STEP_MAX_POS, name="property")
+    DS.assert_bitwise(res)
+
+
+@SETTINGS
+@given(c=step_cases(decode=False))
+def test_prefill_step_is_the_append_then_the_prefill(rope_table, c):
+    """sink_attn_prefill_step against sink_attn_qkv_rope_append followed by
+    sink_attn_prefill: output, LSE and the whole cache bit for bit."""
+    from tests import test_gpu_prefill_step as PS
+    say(f"[case] prefill step {c}")
+    ab, sinks, od = step_inputs(c)
+    res = PS.run_both(ab, rope_table, sinks, c["interleaved"], causal=c["causal"], out_dtype=od,
+                      bias=c["bias"], max_pos=STEP_MAX_POS, name="property")
+    PS.assert_bitwise(res)
