@@ -604,8 +604,10 @@ def traffic_run(torch, sa, device, W):
     256 MiB device-to-device copy three times (the calibration dispatch for
     FETCH_SIZE / WRITE_SIZE), the headline decode's first pass eight times
     (rotating the same four KV copies as the timed run), the causal prefill
-    three times, the long split decode's first pass three times, then the
-    mixed batch's prefill and decode first pass three times each."""
+    three times, the long split decode's first pass three times, the mixed
+    batch's prefill and decode first pass three times each, then the
+    16-token verification batch and the 32-token draft trees three times
+    each."""
     x = torch.ones(256 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     y = torch.empty_like(x)
     for _ in range(3):
@@ -638,6 +640,16 @@ def traffic_run(torch, sa, device, W):
     log(f"[traffic] mixed decode first pass x3: {decode_algorithmic_bytes(mx.decode)} "
         f"algorithmic bytes")
     torch.cuda.synchronize()
+    del r, pdb, mx
+    torch.cuda.empty_cache()
+    for name in ("verify_16tok", "verify_tree_32tok"):
+        vb = W.verify_workload(name)
+        vdb = device.to_device(vb, plan="verify")
+        for _ in range(3):
+            device.run(vdb)
+        torch.cuda.synchronize()
+        log(f"[traffic] {name} x3: {kv_bytes_of(vb)} bytes of KV")
+        del vdb, vb
 
 
 # -------------------------------------------------------------------- main

@@ -921,6 +921,7 @@ sink_attn_status verify_impl(const void* q, const int32_t* qo_indptr, const void
     ta.lse = lse;
     ta.o_part = nullptr;
     ta.lse_part = nullptr;
+    ta.longest_first = batch <= sa::kLongestFirstMaxBatch;
     if (tp.chunks > 1) {
       ta.o_part = static_cast<float*>(workspace);
       ta.lse_part = reinterpret_cast<float*>(

@@ -79,6 +79,10 @@ struct VerifyArgs {
   int32_t col_groups;           // Z: groups of 64 (token, head) columns per (request, KV head)
 };
 
+// Largest batch whose verification jobs the tile kernel orders longest first
+// (four requests per lane of a wave).
+constexpr int32_t kLongestFirstMaxBatch = 256;
+
 struct VerifyTileArgs {
   const uint16_t* q;            // bf16 [total_q, Hq, 64]
   const int32_t* qo_indptr;     // [B+1]
@@ -100,6 +104,7 @@ struct VerifyTileArgs {
   float* lse;                   // [total_q, Hq] or nullptr
   float* o_part;                // [total_q, Hq, max_chunks, 64] (max_chunks > 1)
   float* lse_part;              // [total_q, Hq, max_chunks]
+  int32_t longest_first;        // 1: workgroup i takes the i-th longest job (batch <= kLongestFirstMaxBatch)
 };
 
 struct MergeArgs {

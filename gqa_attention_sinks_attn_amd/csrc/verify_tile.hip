@@ -60,21 +60,141 @@ __device__ __forceinline__ int n_chunks_of(int L, int chunk_tiles) {
   return (tiles + chunk_tiles - 1) / chunk_tiles;
 }
 
+typedef __attribute__((address_space(3))) int lds_int;
+
+// Inclusive prefix sum over the 64 lanes (wave-uniform control flow).
+__device__ __forceinline__ int wave_prefix_sum(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __builtin_amdgcn_ds_bpermute((lane - off) << 2, v);
+    v += lane >= off ? t : 0;
+  }
+  return v;
+}
+
+// Longest-first order of the work items (request b, KV head g, chunk c).
+// An item's length is its chunk's tile count: every chunk but a request's
+// last is full (chunk_tiles tiles); the last holds the rest.  The order:
+// all full chunks, then the last chunks by decreasing length (quantised to
+// 64 levels of chunk_tiles), each group in (request, chunk, KV head) order;
+// items of requests without drafted tokens are left out.  Workgroups are
+// dispatched in index order, so the long items start first and the short
+// ones fill the tail (list scheduling, longest first).  Every wave of the
+// workgroup computes the same item from the request lengths, with no
+// exchange; hist is this wave's 64-entry LDS histogram.  Returns false
+// when rank i is past the last item.
+template <int G>
+__device__ __forceinline__ bool longest_first_item(const VerifyTileArgs& p, int i, int lane,
+                                                   lds_int* hist, int& item) {
+  const int B = p.batch;
+  const int ct = p.chunk_tiles;
+  const int nb = (B + 63) >> 6;
+  int q0[4], q1[4], len[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = 64 * k + lane;
+    const bool in = k < nb && r < B;
+    q0[k] = in ? p.qo_indptr[r] : 0;
+    q1[k] = in ? p.qo_indptr[r + 1] : 0;
+    len[k] = in ? p.kv_len[r] : 0;
+  }
+  // per request (lane, block k): full chunks nf, the last chunk's level lv
+  // (-1 if the request has no partial chunk) and w = items per chunk
+  int nf[4], lv[4], w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int tiles = (len[k] + kTile - 1) / kTile;
+    nf[k] = tiles / ct;
+    const int part = tiles - nf[k] * ct;
+    lv[k] = part > 0 ? (part * 64 - 1) / ct : -1;
+    w[k] = q1[k] > q0[k] ? p.hkv : 0;
+  }
+  int idx = i;
+  bool found = false, full = false;
+  int r_sel = 0, off = 0, w_sel = 1, nf_sel = 0;
+  // full chunks
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (k < nb && !found) {
+      const int c = nf[k] * w[k];
+      const int incl = wave_prefix_sum(c, lane);
+      const int tot = __builtin_amdgcn_readlane(incl, 63);
+      if (idx < tot) {
+        const int ln = __builtin_ctzll(__ballot(incl > idx));
+        off = idx - __builtin_amdgcn_readlane(incl - c, ln);
+        r_sel = 64 * k + ln;
+        w_sel = __builtin_amdgcn_readlane(w[k], ln);
+        nf_sel = __builtin_amdgcn_readlane(nf[k], ln);
+        full = true;
+        found = true;
+      } else {
+        idx -= tot;
+      }
+    }
+  }
+  if (!found) {
+    // last chunks: a histogram of jobs by level, levels taken from the top
+    hist[lane] = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (lv[k] >= 0 && w[k] > 0)
+        __hip_atomic_fetch_add(hist + lv[k], w[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const int h = hist[lane];
+    const int pre = wave_prefix_sum(h, lane);
+    const int total = __builtin_amdgcn_readlane(pre, 63);
+    if (idx >= total) return false;
+    const int above = total - pre;   // jobs on higher levels
+    const int jb = __builtin_ctzll(__ballot(h > 0 && above <= idx && idx < above + h));
+    idx -= __builtin_amdgcn_readlane(above, jb);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k < nb && !found) {
+        const int c = lv[k] == jb ? w[k] : 0;
+        const int incl = wave_prefix_sum(c, lane);
+        const int tot = __builtin_amdgcn_readlane(incl, 63);
+        if (idx < tot) {
+          const int ln = __builtin_ctzll(__ballot(incl > idx));
+          off = idx - __builtin_amdgcn_readlane(incl - c, ln);
+          r_sel = 64 * k + ln;
+          w_sel = __builtin_amdgcn_readlane(w[k], ln);
+          nf_sel = __builtin_amdgcn_readlane(nf[k], ln);
+          found = true;
+        } else {
+          idx -= tot;
+        }
+      }
+    }
+    if (!found) return false;
+  }
+  const int chunk = full ? off / w_sel : nf_sel;
+  const int g = off - (off / w_sel) * w_sel;
+  item = chunk * (p.batch * p.hkv) + r_sel * p.hkv + g;
+  return true;
+}
+
 template <int G, bool TREE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void verify_tile_kernel(VerifyTileArgs p) {
   __shared__ __attribute__((aligned(1024))) char lds_k[kBufs * kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v[kBufs * kTileBytes];
+  __shared__ int lds_hist[4][64];
 
-  // flat index -> (work item = c * B * Hkv + unit, row tile rt): the row
-  // tiles of one item go to the same XCD (workgroups are dealt to the 8 XCDs
-  // round robin), back to back, so their reads of the same pages meet in
-  // that XCD's L2.
+  // flat index -> (item slot, row tile rt): the row tiles of one slot go to
+  // the same XCD (workgroups are dealt to the 8 XCDs round robin), back to
+  // back, so their reads of the same pages meet in that XCD's L2.  Slot ->
+  // work item (c * B * Hkv + unit): longest first for batches of up to 256
+  // requests (longest_first_item), else the slot itself.
   const int n_units = p.batch * p.hkv;
   const int xcd = block_x() & 7;
   const int rest = block_x() >> 3;
   const int rt = rest % p.row_tiles;
-  const int item = (rest / p.row_tiles) * 8 + xcd;
+  const int slot = (rest / p.row_tiles) * 8 + xcd;
+  int item = slot;
+  if (p.longest_first) {
+    const int ln = thread_x() & 63;
+    lds_int* hist = (lds_int*)lds_hist[thread_x() >> 6];
+    if (!longest_first_item<G>(p, slot, ln, hist, item)) return;
+  }
   if (item >= n_units * p.max_chunks) return;
   const int unit = item % n_units;
   const int c = item / n_units;

@@ -280,6 +280,30 @@ def test_verify_tiles_row_tiles_and_group_sizes(hq, hkv, qlens, tree, splits):
     check(f"tiles G={hq // hkv} tree={tree} S={splits}", out, ref, lse, rl, bf16_out=bf16)
 
 
+@pytest.mark.parametrize("B,tree,splits", [(256, True, 0), (257, False, 0), (300, True, 3),
+                                             (64, False, 2), (200, True, 5)])
+def test_verify_tiles_job_orders(B, tree, splits):
+    """Both job orders of the tile kernel: longest first (up to 256 requests;
+    workgroup i computes the i-th longest (request, KV head, chunk, row tile)
+    from the request lengths) and index order (more requests), at the
+    boundary and across it, with ragged drafts (some empty), ragged caches
+    and several chunks: every row of every request is written once."""
+    rng = np.random.default_rng(900 + B + splits)
+    ql = rng.integers(0, 25, size=B)
+    ql[0] = 17
+    L = ql + rng.integers(0, 700, size=B)
+    L[1] = ql[1]                  # a cache that is only its draft
+    L[2] = ql[2] + 2048           # whole chunks and a long last one
+    if tree:
+        b = _tree_batch(int(rng.integers(1 << 30)), list(ql), list(L), 64, 8)
+    else:
+        b = W.make_batch(rng, kind="prefill", qlens=ql, kv_lens=L, hq=64, hkv=8, paged=True,
+                         sinks="normal")
+    out, lse, bf16 = run(b, "verify", splits)
+    ref, rl = oracle.attend(b)
+    check(f"tiles job order B={B} tree={tree} S={splits}", out, ref, lse, rl, bf16_out=bf16)
+
+
 @pytest.mark.parametrize("qlen,tree", [(4, False), (4, True), (40, True), (33, False)])
 def test_verify_without_lse_bf16(qlen, tree):
     """lse = NULL and bf16 output, on the column-group kernel (4 tokens) and
