@@ -311,6 +311,7 @@ sink_attn_status prefill_check(const void* q, const int32_t* qo_indptr, const vo
   a->table = step ? step->table : nullptr;
   a->max_pos = step ? step->max_pos : 0;
   a->interleaved = step ? step->interleaved : 0;
+  a->longest_first = batch <= sa::kPrefillLongestFirstMaxBatch;
   return ok();
 }
 

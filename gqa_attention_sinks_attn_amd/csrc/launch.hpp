@@ -139,7 +139,12 @@ struct PrefillArgs {
   const float* table;           // [max_pos, 64]
   int32_t max_pos;
   int32_t interleaved;
+  int32_t longest_first;        // 1: workgroup i takes the i-th longest query tile (batch <= 128)
 };
+
+// Largest batch whose prefill query tiles the kernel orders longest first
+// (two requests per lane of a wave).
+constexpr int32_t kPrefillLongestFirstMaxBatch = 128;
 
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
 hipError_t launch_decode_balanced(const BalancedDecodeArgs& a, int group, hipStream_t stream);

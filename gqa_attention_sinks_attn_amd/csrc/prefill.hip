@@ -52,22 +52,135 @@ constexpr int kTileBytes = kTile * kD * 2;  // one K or V tile in LDS, rows unpa
 constexpr int kBufs = 3;                    // LDS tile buffers
 constexpr float kFastLimit = 65536.f; // row tile sum that forces a rescale
 
+// Inclusive prefix sum over the 64 lanes (wave-uniform control flow).
+__device__ __forceinline__ int wave_prefix_sum(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __builtin_amdgcn_ds_bpermute((lane - off) << 2, v);
+    v += lane >= off ? t : 0;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+    v = max(v, __builtin_amdgcn_ds_bpermute(((int)__lane_id() ^ off) << 2, v));
+  return v;
+}
+
+// Query tiles of a request whose key-tile count reaches level v or more,
+// i.e. whose key count exceeds x (the level's bound): tile j from the end
+// (j = 0 is the last) sees min(L, L + e - j T) keys when causal, where e
+// pads the first tile (qlen + e = n_tiles T), and all L keys otherwise.
+template <int T>
+__device__ __forceinline__ int tiles_at_or_above(int v, int x, int L, int e, int n_tiles,
+                                                 bool causal) {
+  if (v == 0) return n_tiles;
+  if (L <= x) return 0;
+  if (!causal) return n_tiles;
+  const int jmax = (L + e - x - 1) / T;   // last j >= 1 that still exceeds x
+  return 1 + min(max(jmax, 0), n_tiles - 1);
+}
+
+// Longest-first order of the workgroups (request b, query tile j from the
+// end, KV head g).  A workgroup's length is the number of 64-key tiles it
+// walks.  The order: by that length in 64 levels of the longest request's
+// tile count, from the top; within a level by request, then j, then g, so
+// that consecutive workgroups share a request's keys (and, KV heads being
+// the fastest index, every XCD keeps meeting the same KV heads in its L2).
+// Workgroups are dispatched in index order, so long ones start first and
+// short ones fill the tail.  Every wave computes the same answer from the
+// request lengths, with no exchange.  Returns false past the last
+// workgroup.
+template <int T>
+__device__ __forceinline__ bool longest_first_tile(const PrefillArgs& p, int i, int lane, int& b,
+                                                   int& j, int& g) {
+  const int B = p.batch;
+  int L[2], e[2], nt[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int r = 64 * k + lane;
+    const bool in = r < B;
+    const int q0 = in ? p.qo_indptr[r] : 0;
+    const int q1 = in ? p.qo_indptr[r + 1] : 0;
+    int len = 0;
+    if (in) len = p.kv_len != nullptr ? p.kv_len[r] : p.kv_indptr[r + 1] - p.kv_indptr[r];
+    L[k] = len;
+    nt[k] = (q1 - q0 + T - 1) / T;
+    e[k] = nt[k] * T - (q1 - q0);
+  }
+  const bool causal = p.causal != 0;
+  const int lmax = max(1, wave_max(max((L[0] + kTile - 1) / kTile, (L[1] + kTile - 1) / kTile)));
+  // level v = this lane: key counts above x_lo reach it, above x_hi the next
+  auto bound = [&](int v) {
+    if (v >= 64) return 0x7fffffff;
+    const int64_t lo = ((int64_t)v * lmax + 64) / 64;   // fewest key tiles at level v
+    return (int)(kTile * (lo - 1));
+  };
+  const int x_lo = bound(lane), x_hi = bound(lane + 1);
+  int h = 0;   // workgroups at level `lane`
+  for (int r = 0; r < B; ++r) {
+    const int k = r >> 6, src = r & 63;
+    const int Lr = __builtin_amdgcn_readlane(k ? L[1] : L[0], src);
+    const int er = __builtin_amdgcn_readlane(k ? e[1] : e[0], src);
+    const int nr = __builtin_amdgcn_readlane(k ? nt[1] : nt[0], src);
+    h += tiles_at_or_above<T>(lane, x_lo, Lr, er, nr, causal) -
+         tiles_at_or_above<T>(lane + 1, x_hi, Lr, er, nr, causal);
+  }
+  h *= p.hkv;
+  const int pre = wave_prefix_sum(h, lane);
+  const int total = __builtin_amdgcn_readlane(pre, 63);
+  if (i >= total) return false;
+  const int above = total - pre;           // workgroups on higher levels
+  const int v = __builtin_ctzll(__ballot(h > 0 && above <= i && i < above + h));
+  int idx = i - __builtin_amdgcn_readlane(above, v);
+  const int xv_lo = __builtin_amdgcn_readlane(x_lo, v);
+  const int xv_hi = __builtin_amdgcn_readlane(x_hi, v);
+  // the requests with workgroups at level v, in order
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    if (64 * k < B) {
+      const int first = tiles_at_or_above<T>(v + 1, xv_hi, L[k], e[k], nt[k], causal);
+      const int c = (tiles_at_or_above<T>(v, xv_lo, L[k], e[k], nt[k], causal) - first) * p.hkv;
+      const int incl = wave_prefix_sum(c, lane);
+      const int tot = __builtin_amdgcn_readlane(incl, 63);
+      if (idx < tot) {
+        const int ln = __builtin_ctzll(__ballot(incl > idx));
+        const int off = idx - __builtin_amdgcn_readlane(incl - c, ln);
+        b = 64 * k + ln;
+        j = __builtin_amdgcn_readlane(first, ln) + off / p.hkv;
+        g = off % p.hkv;
+        return true;
+      }
+      idx -= tot;
+    }
+  }
+  return false;
+}
+
 template <int G, bool PAGED, bool STEP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs p) {
   constexpr int T = 256 / G;  // tokens per workgroup
   __shared__ __attribute__((aligned(1024))) char lds_k[kBufs * kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v[kBufs * kTileBytes];
 
-  // Heaviest first: the grid is flat with the round j as its slowest index,
-  // and round j takes the j-th query tile from the end of every request.  A
+  // Heaviest first.  Batches of up to 128 requests: longest_first_tile.
+  // Larger ones: the grid is flat with the round j as its slowest index, and
+  // round j takes the j-th query tile from the end of every request.  A
   // request's last tile sees all of its keys, so round 0 holds the largest
   // workgroup of every request (whatever its cached prefix), and work falls
   // with j.
-  const int units = p.hkv * p.batch;
-  const int wg = block_x();
-  const int j = wg / units;
-  const int g = (wg % units) % p.hkv;
-  const int b = (wg % units) / p.hkv;
+  int j, g, b;
+  if (p.longest_first) {
+    if (!longest_first_tile<T>(p, block_x(), thread_x() & 63, b, j, g)) return;
+  } else {
+    const int units = p.hkv * p.batch;
+    const int wg = block_x();
+    j = wg / units;
+    g = (wg % units) % p.hkv;
+    b = (wg % units) / p.hkv;
+  }
   const int q_begin = p.qo_indptr[b];
   const int qlen = p.qo_indptr[b + 1] - q_begin;
   const int qt = (qlen + T - 1) / T - 1 - j;
