@@ -64,8 +64,8 @@ CSRC = os.path.join(ROOT, "gqa_attention_sinks_attn_amd", "csrc")
 TRAFFIC = {
     "c2": (260_938_798, "decode_balanced.hip", "9a447f3f65222092"),
     "c3": (1_076_430_655, "decode_balanced.hip", "9a447f3f65222092"),
-    "c4": (1_876_238_689, "prefill.hip", "414b58e2ad11b37b"),
-    "c5_prefill": (6_376_976_874, "prefill.hip", "414b58e2ad11b37b"),
+    "c4": (1_878_349_657, "prefill.hip", "e657d3a916caa203"),
+    "c5_prefill": (1_349_909_175, "prefill.hip", "e657d3a916caa203"),
     "c5_decode": (4_355_406_703, "decode_balanced.hip", "9a447f3f65222092"),
 }
 
@@ -243,7 +243,7 @@ def prefill_entry(name, b, ms, steps, traffic=None):
                 roofline=dict(bound="mfma", achieved=round(tfs, 2), peak=BF16_PEAK_TFLOPS,
                               unit="TFLOP/s", frac=round(tfs / BF16_PEAK_TFLOPS, 4),
                               traffic=traffic, kernel=f"prefill_kernel<{b.num_qo_heads // b.num_kv_heads}, "
-                                                      f"{'true' if b.page_indices is not None else 'false'}>"))
+                                                      f"{'true' if b.page_indices is not None else 'false'}, false>"))
 
 
 def bench_workloads(args, torch, sa, device, W):
@@ -255,7 +255,7 @@ def bench_workloads(args, torch, sa, device, W):
     b3 = W.config(3)
     r3 = time_decode(torch, sa, device, b3, steps, warm)
     out["c3_split_decode"] = decode_entry(W.CONFIG_NAMES[3], b3, r3,
-                                          "decode_balanced_kernel<8> (first pass)",
+                                          "decode_balanced_kernel<8, false> (first pass)",
                                           traffic=traffic_of("c3"))
     out["c3_split_decode"]["note"] = (
         "the 32 chunks of the workload are the page ranges of the automatic plan; "
@@ -270,7 +270,7 @@ def bench_workloads(args, torch, sa, device, W):
                                       mx.prefill, pms, steps, traffic=traffic_of("c5_prefill"))
     r5 = time_decode(torch, sa, device, mx.decode, steps, warm)
     out["c5_decode"] = decode_entry(W.CONFIG_NAMES[5] + " -- (ii) decodes", mx.decode, r5,
-                                    "decode_balanced_kernel<8> (first pass)",
+                                    "decode_balanced_kernel<8, false> (first pass)",
                                     traffic=traffic_of("c5_decode"))
     # both calls back to back on one stream, as one step of the mixed batch
     ddb = r5["db"]
@@ -746,7 +746,7 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_of("c2") if balanced else None,
-            "kernel": ("decode_balanced_kernel<8> (first pass)" if balanced
+            "kernel": ("decode_balanced_kernel<8, false> (first pass)" if balanced
                        else "decode_kernel<8> (split-KV partial)"),
             "kernel_ms": round(dec["kern_ms"], 5), "kernel_samples": dec["kern_samples"],
             "algorithmic_bytes": dec["alg_bytes"],
