@@ -51,6 +51,7 @@ constexpr int kTile = 64;            // keys per tile
 constexpr int kTileBytes = kTile * kD * 2;  // one K or V tile in LDS, rows unpadded
 constexpr int kBufs = 3;                    // LDS tile buffers
 constexpr float kFastLimit = 65536.f; // row tile sum that forces a rescale
+constexpr int kOrderLevels = 8;       // length levels of the workgroup order (<= 64)
 
 // Inclusive prefix sum over the 64 lanes (wave-uniform control flow).
 __device__ __forceinline__ int wave_prefix_sum(int v, int lane) {
@@ -85,10 +86,13 @@ __device__ __forceinline__ int tiles_at_or_above(int v, int x, int L, int e, int
 
 // Longest-first order of the workgroups (request b, query tile j from the
 // end, KV head g).  A workgroup's length is the number of 64-key tiles it
-// walks.  The order: by that length in 64 levels of the longest request's
-// tile count, from the top; within a level by request, then j, then g, so
-// that consecutive workgroups share a request's keys (and, KV heads being
-// the fastest index, every XCD keeps meeting the same KV heads in its L2).
+// walks.  The order: by that length in kOrderLevels levels of the longest
+// request's tile count, from the top; within a level by request, then j,
+// then g, so that consecutive workgroups share a request's keys (and, KV
+// heads being the fastest index, every XCD keeps meeting the same KV heads
+// in its L2).  Eight levels rather than finer ones: coarser levels keep
+// more consecutive workgroups on one request (2-3% on equal requests) and
+// still sort a ragged batch's tiles well enough.
 // Workgroups are dispatched in index order, so long ones start first and
 // short ones fill the tail.  Every wave computes the same answer from the
 // request lengths, with no exchange.  Returns false past the last
@@ -114,8 +118,9 @@ __device__ __forceinline__ bool longest_first_tile(const PrefillArgs& p, int i, 
   const int lmax = max(1, wave_max(max((L[0] + kTile - 1) / kTile, (L[1] + kTile - 1) / kTile)));
   // level v = this lane: key counts above x_lo reach it, above x_hi the next
   auto bound = [&](int v) {
-    if (v >= 64) return 0x7fffffff;
-    const int64_t lo = ((int64_t)v * lmax + 64) / 64;   // fewest key tiles at level v
+    if (v >= kOrderLevels) return 0x7fffffff;
+    // fewest key tiles at level v: level(l) = (kOrderLevels l - 1) / lmax
+    const int64_t lo = ((int64_t)v * lmax + kOrderLevels) / kOrderLevels;
     return (int)(kTile * (lo - 1));
   };
   const int x_lo = bound(lane), x_hi = bound(lane + 1);
