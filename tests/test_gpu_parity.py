@@ -253,6 +253,31 @@ def test_prefill_group_sizes_and_layouts(hq, hkv, paged):
     check(f"prefill G={hq // hkv} paged={paged}", out, ref, lse, rl)
 
 
+@pytest.mark.parametrize("B,causal,paged,hq,hkv", [(128, True, True, 64, 8), (129, True, True, 64, 8),
+                                                    (128, False, False, 16, 2), (200, False, True, 16, 1),
+                                                    (97, True, False, 64, 4)])
+def test_prefill_workgroup_orders(B, causal, paged, hq, hkv):
+    """Both workgroup orders of the prefill kernel: longest first (up to 128
+    requests; each workgroup finds its (request, query tile, KV head) from
+    the request lengths) and rounds of query tiles (more requests), on
+    both sides of the boundary, with ragged queries (some empty), ragged
+    prefixes, a request far longer than the rest, and empty caches where
+    the definition allows them: every row of every request written once."""
+    rng = np.random.default_rng(930 + B + int(causal) + hq)
+    ql = rng.integers(0, 70, size=B)
+    ql[0] = 300
+    prefix = rng.integers(0, 400, size=B)
+    prefix[1] = 3000
+    L = ql + prefix
+    if not causal:
+        L[2] = 0                       # no keys: only the sink
+    b = W.make_batch(rng, kind="prefill", qlens=ql, kv_lens=L, hq=hq, hkv=hkv, paged=paged,
+                     causal=causal, sinks="normal")
+    out, lse = gpu_run(b)
+    ref, rl = oracle.attend(b)
+    check(f"prefill order B={B} causal={causal} paged={paged} G={hq // hkv}", out, ref, lse, rl)
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_prefill_chunked_prefix_and_noncausal(causal):
     b = W.make_batch(21, kind="prefill", qlens=[17, 64, 100], kv_lens=[500, 64, 1000], hq=64, hkv=8,
