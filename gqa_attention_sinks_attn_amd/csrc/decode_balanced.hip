@@ -617,7 +617,38 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(BalancedDecodeArgs p
   float ov[kPre];
 #pragma unroll
   for (int j = 0; j < kPre; ++j) ov[j] = p.o_part[(row0 + (int64_t)min(j, n - 1) * p.hq) * kD + lane];
-  // log-sum-exp over the n partials, 64 at a time across lanes
+  if (n <= kPre) {
+    // the usual case: every lane loads the n log-sum-exps itself (the same
+    // addresses in every lane) and merges its dimension with no exchange
+    float lv[kPre];
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) lv[j] = p.lse_part[row0 + (int64_t)min(j, n - 1) * p.hq];
+    float Lm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) Lm = j < n ? fmaxf(Lm, lv[j]) : Lm;
+    float den = 0.f, acc = 0.f;
+    if (Lm != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < kPre; ++j) {
+        float w = (Lm == INFINITY) ? (lv[j] == INFINITY ? 1.f : 0.f) : __expf(lv[j] - Lm);
+        w = j < n ? w : 0.f;
+        den += w;
+        acc += w != 0.f ? w * ov[j] : 0.f;
+      }
+    }
+    const float o = den > 0.f ? acc / den : 0.f;
+    if (p.out_f32) reinterpret_cast<float*>(p.out)[obase] = o;
+    else reinterpret_cast<uint16_t*>(p.out)[obase] = float_to_bf16_bits(o);
+    if (p.lse != nullptr && lane == 0) {
+      float l;
+      if (Lm == -INFINITY) l = -INFINITY;
+      else if (Lm == INFINITY) l = INFINITY;
+      else l = Lm + __logf(den);
+      p.lse[pair] = l;
+    }
+    return;
+  }
+  // more partials: log-sum-exp over them 64 at a time across lanes
   float L = -INFINITY;
   for (int cb = 0; cb < n; cb += 64) {
     const int c = min(cb + lane, n - 1);
