@@ -62,11 +62,11 @@ CSRC = os.path.join(ROOT, "gqa_attention_sinks_attn_amd", "csrc")
 # kernel and by the hash of the sources that build it.  A source change
 # makes the figure stale: it is then reported as null until retaken.
 TRAFFIC = {
-    "c2": (260_938_798, "decode_balanced.hip", "9a447f3f65222092"),
-    "c3": (1_076_430_655, "decode_balanced.hip", "9a447f3f65222092"),
-    "c4": (1_878_349_657, "prefill.hip", "e657d3a916caa203"),
-    "c5_prefill": (1_349_909_175, "prefill.hip", "e657d3a916caa203"),
-    "c5_decode": (4_355_406_703, "decode_balanced.hip", "9a447f3f65222092"),
+    "c2": (260_939_419, "decode_balanced.hip", "eeea2d547a1c646c"),
+    "c3": (1_076_439_260, "decode_balanced.hip", "eeea2d547a1c646c"),
+    "c4": (1_107_463_172, "prefill.hip", "6d00328b91195aad"),
+    "c5_prefill": (1_064_547_851, "prefill.hip", "6d00328b91195aad"),
+    "c5_decode": (4_355_381_223, "decode_balanced.hip", "eeea2d547a1c646c"),
 }
 
 
