@@ -83,7 +83,6 @@ __device__ __forceinline__ int wave_prefix_sum(int v, int lane) {
 // workgroup computes the same item from the request lengths, with no
 // exchange; hist is this wave's 64-entry LDS histogram.  Returns false
 // when rank i is past the last item.
-template <int G>
 __device__ __forceinline__ bool longest_first_item(const VerifyTileArgs& p, int i, int lane,
                                                    lds_int* hist, int& item) {
   const int B = p.batch;
@@ -193,7 +192,7 @@ void verify_tile_kernel(VerifyTileArgs p) {
   if (p.longest_first) {
     const int ln = thread_x() & 63;
     lds_int* hist = (lds_int*)lds_hist[thread_x() >> 6];
-    if (!longest_first_item<G>(p, slot, ln, hist, item)) return;
+    if (!longest_first_item(p, slot, ln, hist, item)) return;
   }
   if (item >= n_units * p.max_chunks) return;
   const int unit = item % n_units;
