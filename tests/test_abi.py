@@ -559,3 +559,26 @@ def test_prefill_step_validation(over, code):
 
 def test_prefill_step_with_no_rows_launches_nothing():
     assert call_prefill_step(total_q=0, max_qlen=0) == OK
+
+
+def test_a_plain_c_caller_builds_and_runs(tmp_path):
+    """The header is C99 and the library links from C: tests/c_abi_consumer.c,
+    compiled with gcc (no C++ runtime of its own) against libsink_attn.so,
+    makes the device-free calls (planning queries, host validation) and
+    checks their results."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    libdir = os.path.dirname(sa.LIB_PATH)
+    exe = str(tmp_path / "c_abi_consumer")
+    build = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                            "-I", os.path.join(ROOT, "include"),
+                            os.path.join(ROOT, "tests", "c_abi_consumer.c"), "-o", exe,
+                            "-L", libdir, "-lsink_attn", f"-Wl,-rpath,{libdir}"],
+                           capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "c consumer ok" in run.stdout
