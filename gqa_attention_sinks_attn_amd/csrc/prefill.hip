@@ -57,7 +57,7 @@ constexpr int kOrderLevels = 8;       // length levels of the workgroup order (<
 __device__ __forceinline__ int wave_prefix_sum(int v, int lane) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int t = __builtin_amdgcn_ds_bpermute((lane - off) << 2, v);
+    const int t = __builtin_amdgcn_ds_bpermute((int)((unsigned)(lane - off) << 2), v);
     v += lane >= off ? t : 0;
   }
   return v;
