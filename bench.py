@@ -36,6 +36,7 @@ counters were taken on; otherwise null.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
     python bench.py --mode traffic   # kernels only, for rocprofv3 --pmc passes
+    python bench.py --mode shapes    # the prefill kernel at three sequence lengths, for --pmc
 """
 from __future__ import annotations
 
@@ -109,9 +110,11 @@ def kv_bytes_of(b) -> int:
 
 
 def prefill_pairs(b) -> int:
-    """Unmasked (query row, head, key) triples of a causal prefill."""
+    """Unmasked (query row, head, key) triples of a prefill (causal or not)."""
     qlens = np.diff(b.qo_indptr).astype(np.int64)
     kvl = b.kv_len.astype(np.int64)
+    if not b.causal:
+        return int((qlens * kvl).sum()) * b.num_qo_heads
     # query t sees keys 0 .. kv_len - qlen + t  ->  sum_t (kv_len - qlen + t + 1)
     per_req = qlens * (kvl - qlens) + qlens * (qlens + 1) // 2
     return int(per_req.sum()) * b.num_qo_heads
@@ -652,6 +655,28 @@ def traffic_run(torch, sa, device, W):
         del vdb, vb
 
 
+def shapes_run(torch, device, W):
+    """Untimed dispatches for counter passes on the prefill kernel across
+    sequence lengths (64 q / 8 KV heads, contiguous cache, seed 7), two each,
+    in this order: causal 8 x 4,096, causal 2 x 16,384, non-causal 8 x 4,096.
+    The same number of workgroups (8,192) with 32.5, 128.5 and 64 key tiles
+    each on average: the counters separate the per-tile cost from the
+    per-workgroup one."""
+    shapes = [("causal 8 x 4096", [4096] * 8, True), ("causal 2 x 16384", [16384] * 2, True),
+              ("non-causal 8 x 4096", [4096] * 8, False)]
+    for name, lens, causal in shapes:
+        b = W.make_batch(7, kind="prefill", qlens=lens, kv_lens=lens, hq=64, hkv=8,
+                         sinks="normal", paged=False, causal=causal)
+        db = device.to_device(b, with_lse=False)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            device.run(db)
+            torch.cuda.synchronize()
+        log(f"[shapes] {name} x2: {prefill_flops(b)} flop per dispatch")
+        del db, b
+        torch.cuda.empty_cache()
+
+
 # -------------------------------------------------------------------- main
 
 def main():
@@ -666,7 +691,8 @@ def main():
                     help="also time the split-KV pair, verification, append and graph batches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
-    ap.add_argument("--mode", choices=["bench", "traffic"], default="bench")
+    ap.add_argument("--mode", choices=["bench", "traffic", "shapes"], default="bench",
+                    help="traffic / shapes: untimed dispatches for rocprofv3 counter passes")
     ap.add_argument("--decode-plan", choices=["balanced", "chunked"], default="balanced",
                     help="decode kernels to time (default: the automatic plan's, balanced)")
     args = ap.parse_args()
@@ -686,6 +712,9 @@ def main():
 
     if args.mode == "traffic":
         traffic_run(torch, sa, device, W)
+        return
+    if args.mode == "shapes":
+        shapes_run(torch, device, W)
         return
 
     log("[bench] decode workload: generating inputs")
