@@ -95,53 +95,80 @@ __device__ __forceinline__ int tiles_at_or_above(int v, int x, int L, int e, int
 // still sort a ragged batch's tiles well enough.
 // Workgroups are dispatched in index order, so long ones start first and
 // short ones fill the tail.  Every wave computes the same answer from the
-// request lengths, with no exchange.  Returns false past the last
-// workgroup.
+// request lengths, with no exchange: each lane holds two requests and counts
+// their tiles at or above every level, a butterfly sums all the levels over
+// the wave at once, and the workgroup's level and request follow from
+// prefix sums, so the cost does not grow with the request count.  Returns
+// false past the last workgroup; otherwise also the chosen request's
+// offsets and lengths, read out of the lanes that loaded them (no second
+// round trip to memory).
+struct RequestSpan {
+  int q_begin, qlen, kv_start, L;
+};
+
 template <int T>
 __device__ __forceinline__ bool longest_first_tile(const PrefillArgs& p, int i, int lane, int& b,
-                                                   int& j, int& g) {
+                                                   int& j, int& g, RequestSpan& rq) {
   const int B = p.batch;
-  int L[2], e[2], nt[2];
+  int L[2], e[2], nt[2], qb[2], ks[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int r = 64 * k + lane;
     const bool in = r < B;
     const int q0 = in ? p.qo_indptr[r] : 0;
     const int q1 = in ? p.qo_indptr[r + 1] : 0;
+    const int k0 = in ? p.kv_indptr[r] : 0;
     int len = 0;
-    if (in) len = p.kv_len != nullptr ? p.kv_len[r] : p.kv_indptr[r + 1] - p.kv_indptr[r];
+    if (in) len = p.kv_len != nullptr ? p.kv_len[r] : p.kv_indptr[r + 1] - k0;
     L[k] = len;
+    qb[k] = q0;
+    ks[k] = k0;
     nt[k] = (q1 - q0 + T - 1) / T;
     e[k] = nt[k] * T - (q1 - q0);
   }
   const bool causal = p.causal != 0;
-  const int lmax = max(1, wave_max(max((L[0] + kTile - 1) / kTile, (L[1] + kTile - 1) / kTile)));
-  // level v = this lane: key counts above x_lo reach it, above x_hi the next
+  const int lmax = __builtin_amdgcn_readfirstlane(
+      max(1, wave_max(max((L[0] + kTile - 1) / kTile, (L[1] + kTile - 1) / kTile))));
+  // Key counts above bound(v) reach level v.
   auto bound = [&](int v) {
     if (v >= kOrderLevels) return 0x7fffffff;
     // fewest key tiles at level v: level(l) = (kOrderLevels l - 1) / lmax
     const int64_t lo = ((int64_t)v * lmax + kOrderLevels) / kOrderLevels;
     return (int)(kTile * (lo - 1));
   };
-  const int x_lo = bound(lane), x_hi = bound(lane + 1);
-  int h = 0;   // workgroups at level `lane`
-  for (int r = 0; r < B; ++r) {
-    const int k = r >> 6, src = r & 63;
-    const int Lr = __builtin_amdgcn_readlane(k ? L[1] : L[0], src);
-    const int er = __builtin_amdgcn_readlane(k ? e[1] : e[0], src);
-    const int nr = __builtin_amdgcn_readlane(k ? nt[1] : nt[0], src);
-    h += tiles_at_or_above<T>(lane, x_lo, Lr, er, nr, causal) -
-         tiles_at_or_above<T>(lane + 1, x_hi, Lr, er, nr, causal);
+  // A[v]: query tiles of the batch at level v or above (A[0] all of them),
+  // each lane counting its two requests, all levels at once, then summed
+  // over the wave.  Level v holds workgroups A[v + 1] hkv .. A[v] hkv - 1.
+  int A[kOrderLevels + 1];
+#pragma unroll
+  for (int v = 0; v < kOrderLevels; ++v) {
+    const int x = bound(v);
+    A[v] = tiles_at_or_above<T>(v, x, L[0], e[0], nt[0], causal);
+    if (B > 64) A[v] += tiles_at_or_above<T>(v, x, L[1], e[1], nt[1], causal);
   }
-  h *= p.hkv;
-  const int pre = wave_prefix_sum(h, lane);
-  const int total = __builtin_amdgcn_readlane(pre, 63);
-  if (i >= total) return false;
-  const int above = total - pre;           // workgroups on higher levels
-  const int v = __builtin_ctzll(__ballot(h > 0 && above <= i && i < above + h));
-  int idx = i - __builtin_amdgcn_readlane(above, v);
-  const int xv_lo = __builtin_amdgcn_readlane(x_lo, v);
-  const int xv_hi = __builtin_amdgcn_readlane(x_hi, v);
+  // butterfly over the lanes, the levels side by side (one LDS round trip
+  // per step for all of them)
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int src = ((int)__lane_id() ^ off) << 2;
+#pragma unroll
+    for (int v = 0; v < kOrderLevels; ++v) A[v] += __builtin_amdgcn_ds_bpermute(src, A[v]);
+  }
+#pragma unroll
+  for (int v = 0; v < kOrderLevels; ++v) A[v] = __builtin_amdgcn_readfirstlane(A[v]);
+  A[kOrderLevels] = 0;
+  if (i >= A[0] * p.hkv) return false;
+  int v = 0;     // the highest level that starts at or before workgroup i
+#pragma unroll
+  for (int u = kOrderLevels - 1; u > 0; --u)
+    if (v == 0 && A[u] * p.hkv > i) v = u;
+  int above = 0;
+#pragma unroll
+  for (int u = 1; u <= kOrderLevels; ++u)
+    if (u == v + 1) above = A[u] * p.hkv;   // workgroups on higher levels
+  int idx = i - above;
+  const int xv_lo = bound(v);
+  const int xv_hi = bound(v + 1);
   // the requests with workgroups at level v, in order
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -156,6 +183,10 @@ __device__ __forceinline__ bool longest_first_tile(const PrefillArgs& p, int i, 
         b = 64 * k + ln;
         j = __builtin_amdgcn_readlane(first, ln) + off / p.hkv;
         g = off % p.hkv;
+        rq.q_begin = __builtin_amdgcn_readlane(qb[k], ln);
+        rq.qlen = __builtin_amdgcn_readlane(nt[k] * T - e[k], ln);
+        rq.kv_start = __builtin_amdgcn_readlane(ks[k], ln);
+        rq.L = __builtin_amdgcn_readlane(L[k], ln);
         return true;
       }
       idx -= tot;
@@ -177,24 +208,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // workgroup of every request (whatever its cached prefix), and work falls
   // with j.
   int j, g, b;
+  RequestSpan rq;
   if (p.longest_first) {
-    if (!longest_first_tile<T>(p, block_x(), thread_x() & 63, b, j, g)) return;
+    if (!longest_first_tile<T>(p, block_x(), thread_x() & 63, b, j, g, rq)) return;
   } else {
     const int units = p.hkv * p.batch;
     const int wg = block_x();
     j = wg / units;
     g = (wg % units) % p.hkv;
     b = (wg % units) / p.hkv;
+    rq.q_begin = p.qo_indptr[b];
+    rq.qlen = p.qo_indptr[b + 1] - rq.q_begin;
+    rq.kv_start = p.kv_indptr[b];
+    rq.L = p.kv_len != nullptr ? p.kv_len[b] : p.kv_indptr[b + 1] - rq.kv_start;
   }
-  const int q_begin = p.qo_indptr[b];
-  const int qlen = p.qo_indptr[b + 1] - q_begin;
+  const int q_begin = rq.q_begin;
+  const int qlen = rq.qlen;
   const int qt = (qlen + T - 1) / T - 1 - j;
   if (qt < 0) return;
   const int t0 = qt * T;
-  const int kv_start = p.kv_indptr[b];
-  int L;
-  if (p.kv_len != nullptr) L = p.kv_len[b];
-  else L = p.kv_indptr[b + 1] - kv_start;
+  const int kv_start = rq.kv_start;
+  const int L = rq.L;
   const int pos_base = L - qlen;  // absolute position of token 0
 
   const int tid = thread_x();
@@ -301,23 +335,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // on the matrix core into dk: in every lane l, element 0 (and 2) holds row
   // l % 16 of the column block and element 1 (and 3) row 16 + l % 16, so a
   // lane's own row r = l % 32 is element r / 16 of its own dk. ----
-  float m[2], d[2];
+  // (The sinks are read once the first tile is in flight, below.)
+  float m[2] = {-INFINITY, -INFINITY}, d[2] = {0.f, 0.f};
   f32x4 dk[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   f32x16 o[2][2];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    m[cb] = -INFINITY;
-    d[cb] = 0.f;
-    if (p.sinks != nullptr) {
-      const float sg = p.sinks[head[cb]];
-      m[cb] = sg * kLog2e;
-      d[cb] = (hh == 0 && sg != -INFINITY) ? 1.f : 0.f;
-    }
+  for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int j = 0; j < 16; ++j) o[cb][db][j] = 0.f;
-  }
 
   // ---- tile loader.  A tile's K and V go straight from global memory
   // into LDS (load_lds16), 1 KiB blocks of eight key rows (key row r in
@@ -408,10 +435,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   int ids = 0;
   if constexpr (PAGED) ids = load_ids(0);
-  // the prologue's own global loads complete here, not inside the loop
-  asm volatile("" ::"v"(bq[0][0]), "v"(bq[0][1]), "v"(bq[0][2]), "v"(bq[0][3]), "v"(bq[1][0]),
-               "v"(bq[1][1]), "v"(bq[1][2]), "v"(bq[1][3]));
   if (n_tiles > 0) issue(0, 0, __builtin_amdgcn_readlane(ids, 0));
+  if (p.sinks != nullptr) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float sg = p.sinks[head[cb]];
+      m[cb] = sg * kLog2e;
+      d[cb] = (hh == 0 && sg != -INFINITY) ? 1.f : 0.f;
+    }
+  }
+  // The prologue's own global loads (queries, sinks) complete here, not
+  // inside the loop.  The first tile is already in flight, so its latency
+  // overlaps theirs; the compiler, which does not count the tile loads,
+  // waits for everything issued so far, then the second tile goes out.
+  asm volatile("" ::"v"(bq[0][0]), "v"(bq[0][1]), "v"(bq[0][2]), "v"(bq[0][3]), "v"(bq[1][0]),
+               "v"(bq[1][1]), "v"(bq[1][2]), "v"(bq[1][3]), "v"(m[0]), "v"(m[1]));
   if (n_tiles > 1) issue(1, 1, __builtin_amdgcn_readlane(ids, 1));
 
   const float sl2 = p.scale_log2;
