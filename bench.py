@@ -56,6 +56,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 KV_COPIES = 4                  # rotated KV pools: 4 x 269 MB > 256 MB last-level cache
 EVENT_EVERY = 4                # timed decode steps between two sampled first-pass launches
+BURST = 32                     # back-to-back first-pass launches timed as one block
 CSRC = os.path.join(ROOT, "gqa_attention_sinks_attn_amd", "csrc")
 
 # HBM bytes per dispatch (FETCH_SIZE + WRITE_SIZE, scaled by the 256 MiB
@@ -127,10 +128,14 @@ def prefill_flops(b) -> int:
 # ------------------------------------------------------------------ decode
 
 def time_decode(torch, sa, device, b, steps, warmup, balanced=True, kv_copies=1,
-                event_every=1):
-    """Times the decode of batch b: the first pass (events around every
-    `event_every`-th launch, on the stream it runs on) and the whole step
-    (first pass + finish, events around the timed region)."""
+                event_every=1, burst=BURST):
+    """Times the decode of batch b: the whole step (first pass + finish,
+    events around the timed region of `steps` steps) and the first pass:
+    events around a block of `burst` back-to-back first-pass launches on the
+    rotated KV copies, right after the steps (the kernel's average launch
+    duration, as a kernel trace reports it), and, for reference, events
+    around every `event_every`-th launch inside the steps (each such pair
+    adds the event packets' own few microseconds to a ~50 us launch)."""
     db = device.to_device(b, plan="balanced" if balanced else "chunked")
     B, Hq, D = db.batch, db.num_qo_heads, db.head_dim
     out_code = sa.F32 if db.out.dtype == torch.float32 else sa.BF16
@@ -192,8 +197,21 @@ def time_decode(torch, sa, device, b, steps, warmup, balanced=True, kv_copies=1,
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
-    kern_ms = float(np.mean([a.elapsed_time(c) for a, c in evs.values()]))
-    res = dict(db=db, plan=plan, ms_step=ms_step, kern_ms=kern_ms, kern_samples=len(evs),
+    single_ms = float(np.mean([a.elapsed_time(c) for a, c in evs.values()]))
+    kern_ms = single_ms
+    if burst > 0:
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for i in range(burst):
+            first(ks[(steps + i) % kv_copies], vs[(steps + i) % kv_copies])
+        b1.record()
+        second()   # leave the outputs of a whole step behind
+        torch.cuda.synchronize()
+        kern_ms = b0.elapsed_time(b1) / burst
+    res = dict(db=db, plan=plan, ms_step=ms_step, kern_ms=kern_ms,
+               kern_samples=burst if burst > 0 else len(evs),
+               kern_single_ms=single_ms, kern_single_samples=len(evs),
                kv_bytes=kv_bytes_of(b), alg_bytes=decode_algorithmic_bytes(b),
                first=first, ks=ks, vs=vs)
     return res
@@ -214,7 +232,11 @@ def decode_entry(name, b, r, kernel, traffic=None):
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": kernel, "kernel_ms": round(r["kern_ms"], 5),
-            "kernel_samples": r["kern_samples"], "algorithmic_bytes": r["alg_bytes"],
+            "kernel_samples": r["kern_samples"],
+            "kernel_timing": f"HIP events around {r['kern_samples']} back-to-back first-pass "
+                             "launches on rotated KV copies (cache-cold), after the timed steps",
+            "kernel_ms_single_brackets": round(r["kern_single_ms"], 5),
+            "algorithmic_bytes": r["alg_bytes"],
         },
     }
 
@@ -619,7 +641,7 @@ def traffic_run(torch, sa, device, W):
     log(f"[traffic] copy: {x.numel() * 4} bytes read and written per dispatch")
     del x, y
     b = W.config(2)
-    r = time_decode(torch, sa, device, b, steps=8, warmup=0, kv_copies=KV_COPIES)
+    r = time_decode(torch, sa, device, b, steps=8, warmup=0, kv_copies=KV_COPIES, burst=0)
     log(f"[traffic] decode first pass x8: {decode_algorithmic_bytes(b)} algorithmic bytes")
     del r
     pb = W.config(4)
@@ -630,7 +652,7 @@ def traffic_run(torch, sa, device, W):
     log(f"[traffic] prefill x3: {prefill_flops(pb)} flop per dispatch")
     del pdb, pb
     b3 = W.config(3)
-    r = time_decode(torch, sa, device, b3, steps=3, warmup=0)
+    r = time_decode(torch, sa, device, b3, steps=3, warmup=0, burst=0)
     log(f"[traffic] long decode first pass x3: {decode_algorithmic_bytes(b3)} algorithmic bytes")
     del r, b3
     mx = W.config(5)
@@ -639,7 +661,7 @@ def traffic_run(torch, sa, device, W):
         device.run(pdb)
     torch.cuda.synchronize()
     log(f"[traffic] mixed prefill x3: {prefill_flops(mx.prefill)} flop per dispatch")
-    r = time_decode(torch, sa, device, mx.decode, steps=3, warmup=0)
+    r = time_decode(torch, sa, device, mx.decode, steps=3, warmup=0, burst=0)
     log(f"[traffic] mixed decode first pass x3: {decode_algorithmic_bytes(mx.decode)} "
         f"algorithmic bytes")
     torch.cuda.synchronize()
@@ -778,6 +800,9 @@ def main():
             "kernel": ("decode_balanced_kernel<8, false> (first pass)" if balanced
                        else "decode_kernel<8> (split-KV partial)"),
             "kernel_ms": round(dec["kern_ms"], 5), "kernel_samples": dec["kern_samples"],
+            "kernel_timing": f"HIP events around {dec['kern_samples']} back-to-back first-pass "
+                             f"launches on the {KV_COPIES} rotated KV copies, after the timed steps",
+            "kernel_ms_single_brackets": round(dec["kern_single_ms"], 5),
             "algorithmic_bytes": dec["alg_bytes"],
         },
         "cpu_baseline": cpu,
