@@ -481,6 +481,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int vread = 512 * hh + 64 * ((lane & 15) >> 2) + 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) +
                     8 * (lane & 1);
 
+  // Every scalar load of the prologue completes here.  Left pending, it
+  // would make the compiler count the loop's LDS reads as if they could
+  // return out of order, and wait for all eight K reads of a tile before its
+  // first product (s_waitcnt lgkmcnt(0) in every tile).
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), no vector-memory wait
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int buf = kt % kBufs;
     // this wave's part of tile kt has landed (tile kt + 1 may be in
@@ -611,6 +616,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           sacc[kb][0] = mfma32(ko[s][kb], bq[0][s], s == 0 ? zero16 : sacc[kb][0]);
+      // the reads go out a few ahead of the products that consume them, so
+      // each product waits for its own operand only
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // DS read
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // MFMA
       if (edge) mask(0);
       // (2) S^T of column block 1 on the matrix core while the vector unit
       //     exponentiates block 0; block 0's row sums go to the matrix core
