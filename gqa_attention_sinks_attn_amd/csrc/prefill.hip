@@ -40,6 +40,8 @@
 //     of each request, so the tile that sees the most keys of every
 //     (request, KV head) pair starts first (with or without a cached
 //     prefix) and the short ones fill the tail.
+#include <climits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -53,21 +55,29 @@ constexpr int kBufs = 3;                    // LDS tile buffers
 constexpr float kFastLimit = 65536.f; // row tile sum that forces a rescale
 constexpr int kOrderLevels = 8;       // length levels of the workgroup order (<= 64)
 
-// Inclusive prefix sum over the 64 lanes (wave-uniform control flow).
-__device__ __forceinline__ int wave_prefix_sum(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __builtin_amdgcn_ds_bpermute((int)((unsigned)(lane - off) << 2), v);
-    v += lane >= off ? t : 0;
-  }
+// Inclusive scans over the 64 lanes on the vector unit (wave-uniform control
+// flow): shifts by 1, 2, 4 and 8 lanes inside each 16-lane row, then lane 15
+// of each row added into the next row and lane 31 into the upper two rows
+// (the row_shr and row_bcast forms of DPP).  Lanes without a source add the
+// identity.  No LDS round trips, unlike a ds_bpermute ladder.
+template <class Op>
+__device__ __forceinline__ int wave_scan(int v, Op op, int identity) {
+  v = op(v, __builtin_amdgcn_update_dpp(identity, v, 0x111, 0xf, 0xf, false));   // row_shr:1
+  v = op(v, __builtin_amdgcn_update_dpp(identity, v, 0x112, 0xf, 0xf, false));   // row_shr:2
+  v = op(v, __builtin_amdgcn_update_dpp(identity, v, 0x114, 0xf, 0xf, false));   // row_shr:4
+  v = op(v, __builtin_amdgcn_update_dpp(identity, v, 0x118, 0xf, 0xf, false));   // row_shr:8
+  v = op(v, __builtin_amdgcn_update_dpp(identity, v, 0x142, 0xa, 0xf, false));   // row_bcast:15
+  v = op(v, __builtin_amdgcn_update_dpp(identity, v, 0x143, 0xc, 0xf, false));   // row_bcast:31
   return v;
 }
 
+__device__ __forceinline__ int wave_prefix_sum(int v, int) {
+  return wave_scan(v, [](int a, int b) { return a + b; }, 0);
+}
+
+// Maximum over the wave, wave-uniform.
 __device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1)
-    v = max(v, __builtin_amdgcn_ds_bpermute(((int)__lane_id() ^ off) << 2, v));
-  return v;
+  return __builtin_amdgcn_readlane(wave_scan(v, [](int a, int b) { return max(a, b); }, INT_MIN), 63);
 }
 
 // Query tiles of a request whose key-tile count reaches level v or more,
@@ -146,16 +156,9 @@ __device__ __forceinline__ bool longest_first_tile(const PrefillArgs& p, int i, 
     A[v] = tiles_at_or_above<T>(v, x, L[0], e[0], nt[0], causal);
     if (B > 64) A[v] += tiles_at_or_above<T>(v, x, L[1], e[1], nt[1], causal);
   }
-  // butterfly over the lanes, the levels side by side (one LDS round trip
-  // per step for all of them)
+  // summed over the lanes, the levels side by side
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const int src = ((int)__lane_id() ^ off) << 2;
-#pragma unroll
-    for (int v = 0; v < kOrderLevels; ++v) A[v] += __builtin_amdgcn_ds_bpermute(src, A[v]);
-  }
-#pragma unroll
-  for (int v = 0; v < kOrderLevels; ++v) A[v] = __builtin_amdgcn_readfirstlane(A[v]);
+  for (int v = 0; v < kOrderLevels; ++v) A[v] = __builtin_amdgcn_readlane(wave_prefix_sum(A[v], lane), 63);
   A[kOrderLevels] = 0;
   if (i >= A[0] * p.hkv) return false;
   int v = 0;     // the highest level that starts at or before workgroup i

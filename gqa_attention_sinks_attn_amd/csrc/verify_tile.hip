@@ -62,13 +62,18 @@ __device__ __forceinline__ int n_chunks_of(int L, int chunk_tiles) {
 
 typedef __attribute__((address_space(3))) int lds_int;
 
-// Inclusive prefix sum over the 64 lanes (wave-uniform control flow).
-__device__ __forceinline__ int wave_prefix_sum(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __builtin_amdgcn_ds_bpermute((int)((unsigned)(lane - off) << 2), v);
-    v += lane >= off ? t : 0;
-  }
+// Inclusive prefix sum over the 64 lanes on the vector unit (wave-uniform
+// control flow): shifts by 1, 2, 4 and 8 lanes inside each 16-lane row, then
+// lane 15 of each row added into the next row and lane 31 into the upper two
+// rows (the row_shr and row_bcast forms of DPP); lanes without a source add
+// 0.  No LDS round trips, unlike a ds_bpermute ladder.
+__device__ __forceinline__ int wave_prefix_sum(int v, int) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
   return v;
 }
 
