@@ -453,6 +453,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // waits for everything issued so far, then the second tile goes out.
   asm volatile("" ::"v"(bq[0][0]), "v"(bq[0][1]), "v"(bq[0][2]), "v"(bq[0][3]), "v"(bq[1][0]),
                "v"(bq[1][1]), "v"(bq[1][2]), "v"(bq[1][3]), "v"(m[0]), "v"(m[1]));
+  // The negated reference the fast path subtracts (0 for a row without one,
+  // whose tile then takes the slow path anyway), refreshed where m changes.
+  float nm[2];
+  auto refresh_ref = [&](int cb) { nm[cb] = (m[cb] == -INFINITY) ? 0.f : -m[cb]; };
+  refresh_ref(0);
+  refresh_ref(1);
   if (n_tiles > 1) issue(1, 1, __builtin_amdgcn_readlane(ids, 1));
 
   const float sl2 = p.scale_log2;
@@ -555,7 +561,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           pk[cb][kb][hf][q] = pack_bf16x2(e0, e1);
         }
       };
-      auto neg_ref = [&](int cb) { return (m[cb] == -INFINITY) ? 0.f : -m[cb]; };
       auto pb_of = [&](int cb, int kb, int hf) {
         return as_bf16x8(u32x4{pk[cb][kb][hf][0], pk[cb][kb][hf][1], pk[cb][kb][hf][2], pk[cb][kb][hf][3]});
       };
@@ -599,8 +604,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           o[cb][0] *= alpha;
           o[cb][1] *= alpha;
           m[cb] = m_new;
+          refresh_ref(cb);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) expo4(cb, neg_ref(cb), i >> 2, (i >> 1) & 1, i & 1);
+          for (int i = 0; i < 8; ++i) expo4(cb, nm[cb], i >> 2, (i >> 1) & 1, i & 1);
           rs = row_sums(cb);
         }
         dk[cb][0] += rs[0];
@@ -633,13 +639,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       //     exponentiates block 0; block 0's row sums go to the matrix core
       //     as each 16-key slice of P is packed.
       {
-        const float nm = neg_ref(0);
+        const float nmr = nm[0];
         f32x4 rs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int s = i >> 1, kb = i & 1;
           sacc[kb][1] = mfma32(ko[s][kb], bq[1][s], s == 0 ? zero16 : sacc[kb][1]);
-          expo4(0, nm, i >> 2, (i >> 1) & 1, i & 1);
+          expo4(0, nmr, i >> 2, (i >> 1) & 1, i & 1);
           if (i & 1) rs = mfma16(ones_sel, pb_of(0, i >> 2, (i >> 1) & 1), rs);
         }
 #pragma unroll
@@ -656,7 +662,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       //     exponentials cover their latency), and serve both blocks.
       bf16x8 vo[2][2][2];
       {
-        const float nm = neg_ref(1);
+        const float nmr = nm[1];
         f32x4 rs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 8; ++i) vo[i >> 2][(i >> 1) & 1][i & 1] = vop(i >> 2, (i >> 1) & 1, i & 1);
@@ -664,7 +670,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int i = 0; i < 8; ++i) {
           const int kb = i >> 2, hf = (i >> 1) & 1, db = i & 1;
           o[0][db] = mfma32(vo[kb][hf][db], pb_of(0, kb, hf), o[0][db]);
-          expo4(1, nm, i >> 2, (i >> 1) & 1, i & 1);
+          expo4(1, nmr, i >> 2, (i >> 1) & 1, i & 1);
           if (i & 1) rs = mfma16(ones_sel, pb_of(1, i >> 2, (i >> 1) & 1), rs);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);    // DS read: all of V^T
