@@ -66,8 +66,8 @@ CSRC = os.path.join(ROOT, "gqa_attention_sinks_attn_amd", "csrc")
 TRAFFIC = {
     "c2": (260_939_419, "decode_balanced.hip", "eeea2d547a1c646c"),
     "c3": (1_076_439_260, "decode_balanced.hip", "eeea2d547a1c646c"),
-    "c4": (1_107_497_250, "prefill.hip", "bb0774aafadd651e"),
-    "c5_prefill": (1_065_598_565, "prefill.hip", "bb0774aafadd651e"),
+    "c4": (1_107_493_841, "prefill.hip", "c3f96a6225b93810"),
+    "c5_prefill": (1_066_478_760, "prefill.hip", "c3f96a6225b93810"),
     "c5_decode": (4_355_381_223, "decode_balanced.hip", "eeea2d547a1c646c"),
 }
 
